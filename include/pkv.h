@@ -1,0 +1,162 @@
+/*
+ * pkv.h -- C ABI of the paged-KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * The KV cache of every sequence is split into fixed 16-token blocks that are
+ * logically contiguous and physically scattered; a per-sequence block table
+ * maps logical blocks to physical blocks, the decode kernel walks a
+ * sequence's logical blocks through that table, and new tokens enter the
+ * cache through a slot mapping.
+ *   Sources: ipipp.com vLLM/PagedAttention article (2026-09-14), section 二
+ *   "PagedAttention分页原理深度剖析" (16-token blocks, block table, block-wise
+ *   kernel traversal); bytelighting wiki "vLLM", 核心机制 / 工作原理,
+ *   "Flattened 布局与 slot_mapping" (slot mapping); ai-maas.com "vLLM 深读：
+ *   用 PagedAttention 撑起高并发 LLM 推理", section 先看浪费在哪里 (physically
+ *   scattered blocks, prefixes shared by pointing at the same blocks).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *    owns and allocates every buffer; the library allocates nothing and keeps
+ *    no state between calls (it is reentrant).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; calls on one
+ *    stream run in order (a write followed by a decode sees the write).
+ *  - Arguments are validated on the host before anything is launched; the
+ *    return value is a pkv_status.  The library never reads device arrays on
+ *    the host (that would synchronise), so their CONTENTS are not validated
+ *    up front.  Instead the kernels never touch memory outside the buffers
+ *    the sizes describe: a table entry outside [0, num_blocks) makes its
+ *    block count as empty, a length outside [0, max_blocks_per_seq*16] is
+ *    clamped into that range, a slot outside [-1, num_blocks*16) is skipped.
+ *    Results for such inputs are unspecified (but memory-safe).
+ *  - All device pointers must be 16-byte aligned (PKV_ERR_ALIGNMENT).
+ *  - block_size must be 16; head_dim must be 64 or 128; num_heads must be a
+ *    multiple of num_kv_heads.  Supported (q, cache) dtype pairs for decode:
+ *    (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ *
+ * Pool layout (K and V pools are separate and identical in shape):
+ *    cache[num_blocks][num_kv_heads][block_size][head_dim]
+ * Slot `sl` is offset sl % block_size of physical block sl / block_size.
+ * fp8 pools hold OCP E4M3 codes (bias 7, max 448, no infinities); one fp32
+ * scale per pool: value = decode(code) * k_scale (K) or * v_scale (V).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_dtype {
+    PKV_DTYPE_F32 = 0,      /* IEEE binary32 */
+    PKV_DTYPE_BF16 = 1,     /* bfloat16 */
+    PKV_DTYPE_FP8_E4M3 = 2  /* OCP E4M3 code, one byte */
+} pkv_dtype;
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = 1,  /* a size, scale or pointer argument is out of range */
+    PKV_ERR_UNSUPPORTED = 2,  /* a valid but unimplemented combination (dtype pair, head_dim, block_size) */
+    PKV_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned */
+    PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than paged_attention_workspace_bytes() */
+    PKV_ERR_HIP = 5           /* the HIP runtime reported an error while launching */
+} pkv_status;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int pkv_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (host). */
+const char* pkv_status_string(int status);
+
+/*
+ * paged_kv_write -- store new tokens' K and V into the paged pools.
+ *   Source: bytelighting wiki "vLLM", "Flattened 布局与 slot_mapping" (each
+ *   token's logical position is sent to a physical slot); ipipp.com article
+ *   §二 (16 tokens per block).
+ *
+ * k_new, v_new   [num_tokens][num_kv_heads][head_dim] in in_dtype.
+ * k_cache,
+ * v_cache        [num_blocks][num_kv_heads][block_size][head_dim] in cache_dtype.
+ * slot_mapping   [num_tokens] int32: slot of token i, or -1 to skip it.
+ *                Slots must be distinct (a repeated slot gives an unspecified
+ *                one of the written values).
+ * k_scale,
+ * v_scale        used only when cache_dtype is FP8_E4M3 (must be finite and
+ *                > 0 then): the code stored is the round-to-nearest-even,
+ *                saturating (|y| >= 448 -> +-448, NaN -> NaN) E4M3 encoding of
+ *                the fp32 quotient y = x / scale.
+ * Supported: in_dtype == cache_dtype (bits copied), or cache FP8_E4M3 with
+ * in_dtype F32 or BF16 (quantised).  num_tokens == 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG (negative sizes, NULL pointers with
+ * num_tokens > 0, bad scales, num_blocks*block_size >= 2^31),
+ * PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT, PKV_ERR_HIP.
+ */
+int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
+                   void* k_cache, void* v_cache, int cache_dtype,
+                   const int32_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t num_blocks, float k_scale, float v_scale,
+                   void* stream);
+
+/*
+ * paged_attention_workspace_bytes -- bytes of device workspace that
+ * paged_attention_decode needs for these sizes (host; 0 when every sequence
+ * fits one partition, i.e. max_blocks_per_seq*block_size <= partition size).
+ * partition_size as in paged_attention_decode (0 = the default).  Returns 0
+ * for arguments paged_attention_decode would reject.
+ */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends over its
+ * paged context:
+ *   out[s][h][:] = sum_t softmax_t(scale * q[s][h] . k_t) v_t,  t in [0, L_s)
+ * with L_s = context_lens[s] and k_t, v_t read from physical block
+ * block_table[s][t / 16] at offset t % 16, KV head h / (num_heads/num_kv_heads).
+ *   Source: ipipp.com article §二 (for each logical block the kernel looks up
+ *   the table and reads that block's K/V; the result equals attention over
+ *   contiguous memory); bytelighting wiki "vLLM", 参考来源 (online softmax).
+ *
+ * out            [num_seqs][num_heads][head_dim] in q_dtype (round to nearest even).
+ * q              [num_seqs][num_heads][head_dim] in q_dtype.
+ * k_cache,
+ * v_cache        pools as above, cache_dtype.
+ * block_table    [num_seqs][max_blocks_per_seq] int32; entries at and after
+ *                ceil(L_s/16) are never read (pad them with -1).
+ * context_lens   [num_seqs] int32, each in [0, max_blocks_per_seq*block_size];
+ *                L_s == 0 gives an all-zero output row.  L_s counts the token
+ *                written in the current step.
+ * scale          softmax scale (typically 1/sqrt(head_dim)).
+ * k_scale,
+ * v_scale        fp8 pool scales (ignored for F32/BF16 pools).
+ * partition_size tokens per work unit along the context (split-K): 0 = the
+ *                default (512), otherwise a positive multiple of 16.  When a
+ *                sequence spans several partitions each writes a partial
+ *                result to the workspace and a second kernel merges them.
+ * workspace      device buffer of >= paged_attention_workspace_bytes(...)
+ *                bytes (may be NULL when that is 0), owned by the caller,
+ *                contents need no initialisation.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT,
+ * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  num_seqs == 0 is a no-op.
+ */
+int paged_attention_decode(void* out,
+                           const void* q, int q_dtype,
+                           const void* k_cache, const void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,1 +1,146 @@
-"""paged_kv_cache_369_amd: paged-KV-cache decode attention for MI355X (gfx950)."""
+"""paged_kv_cache_369_amd -- paged-KV-cache decode attention for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/pkv.h`` (library
+``libpkv.so`` next to this file).  The functions carry the C names, take torch
+tensors that already live on the GPU, and only marshal arguments: every step
+of the computation runs in the library's HIP kernels on torch's current
+stream.  There is no CPU fallback: if the library is missing the first call
+raises.
+
+    paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale=1, v_scale=1)
+    paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, scale, ...)
+    paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, ...)
+
+Layouts: new tokens ``[T, H_kv, D]``; pools ``[num_blocks, H_kv, 16, D]``
+(fp8 pools as ``torch.uint8`` or ``torch.float8_e4m3fn``); ``q`` and ``out``
+``[B, H_q, D]``; ``block_table`` ``[B, max_blocks]`` int32 (-1 padded);
+``context_lens`` ``[B]`` int32; ``slot_mapping`` ``[T]`` int32 (-1 = skip).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
+           "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "DEFAULT_PARTITION"]
+
+BLOCK_SIZE = 16
+DEFAULT_PARTITION = 512
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (pkv status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"HIP library {_LIB_PATH} is not built; run `python -m paged_kv_cache_369_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.pkv_abi_version.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.paged_kv_write.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, i32, i32, i32, i32, f32, f32, p]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_workspace_bytes.restype = sz
+    lib.paged_attention_decode.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p,
+                                           i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def pkv_abi_version() -> int:
+    return _load().pkv_abi_version()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return 0
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return 2
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PkvError(status, f"{what}: {_load().pkv_status_string(status).decode()}")
+
+
+def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0,
+                   stream=None) -> None:
+    """Store new tokens' K/V at their slots (copy, or quantise into an fp8 pool)."""
+    lib = _load()
+    T, H, D = k_new.shape
+    NB, Hc, BS, Dc = k_cache.shape
+    if (Hc, Dc) != (H, D) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new tokens and pools")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = lib.paged_kv_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
+                            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                            _dev(slot_mapping, "slot_mapping"), T, H, D, BS, NB,
+                            float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "paged_kv_write")
+
+
+def paged_attention_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_blocks_per_seq: int,
+                                    block_size: int = BLOCK_SIZE, partition_size: int = 0) -> int:
+    return int(_load().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                                       block_size, partition_size))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float,
+                           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                           workspace=None, stream=None) -> None:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the paged context of sequence s."""
+    import torch
+    lib = _load()
+    B, Hq, D = q.shape
+    NB, Hkv, BS, Dc = k_cache.shape
+    if out.shape != q.shape or Dc != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and context_lens [B]")
+    MB = block_table.shape[1]
+    need = paged_attention_workspace_bytes(B, Hq, D, MB, BS, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attention_decode(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),
+                                    _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                                    _dev(block_table, "block_table"), MB, _dev(context_lens, "context_lens"),
+                                    B, Hq, Hkv, D, BS, NB, float(scale), float(k_scale), float(v_scale),
+                                    int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "paged_attention_decode")

@@ -1,0 +1,164 @@
+// C ABI of the paged-KV decode library: host-side validation and dispatch.
+// Declarations and the argument contract are in include/pkv.h.
+#include "../../include/pkv.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool known_dtype(int dt) { return dt == PKV_DTYPE_F32 || dt == PKV_DTYPE_BF16 || dt == PKV_DTYPE_FP8_E4M3; }
+
+int part_tokens(int32_t partition_size) { return partition_size == 0 ? pkv::kDefaultPartition : partition_size; }
+
+// Partitions per sequence row of the workspace, or -1 for a bad partition size.
+int64_t max_parts(int32_t max_blocks_per_seq, int32_t partition_size) {
+    if (partition_size < 0 || (partition_size % pkv::kBlockTokens) != 0) return -1;
+    const int64_t pb = part_tokens(partition_size) / pkv::kBlockTokens;
+    const int64_t mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
+    return (mb + pb - 1) / pb;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return kAbiVersion; }
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported combination";
+    case PKV_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
+                   void* k_cache, void* v_cache, int cache_dtype,
+                   const int32_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t num_blocks, float k_scale, float v_scale,
+                   void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
+        return PKV_ERR_INVALID_ARG;
+    if (!known_dtype(in_dtype) || !known_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+    if (block_size != pkv::kBlockTokens || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+    const bool quant = in_dtype != cache_dtype;
+    if (quant && !(cache_dtype == PKV_DTYPE_FP8_E4M3 && (in_dtype == PKV_DTYPE_F32 || in_dtype == PKV_DTYPE_BF16)))
+        return PKV_ERR_UNSUPPORTED;
+    if (quant && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return PKV_ERR_INVALID_ARG;
+    if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(slot_mapping, 4))
+        return PKV_ERR_ALIGNMENT;
+    if (num_blocks == 0) return PKV_OK;  // every slot is out of range: nothing can be written
+
+    pkv::WriteArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.num_slots = num_blocks * pkv::kBlockTokens;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    const hipError_t e = pkv::launch_kv_write(in_dtype, cache_dtype, head_dim, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq < 0 ||
+        block_size != pkv::kBlockTokens)
+        return 0;
+    const int64_t mp = max_parts(max_blocks_per_seq, partition_size);
+    if (mp <= 1) return 0;
+    return size_t(num_seqs) * size_t(num_heads) * size_t(mp) * size_t(head_dim + 2) * sizeof(float);
+}
+
+int paged_attention_decode(void* out,
+                           const void* q, int q_dtype,
+                           const void* k_cache, const void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks < 0 || max_blocks_per_seq < 0)
+        return PKV_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+    if (!known_dtype(q_dtype) || !known_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+    if (partition_size < 0 || partition_size % pkv::kBlockTokens != 0) return PKV_ERR_INVALID_ARG;
+    if (block_size != pkv::kBlockTokens || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+    const bool pair_ok = (q_dtype == PKV_DTYPE_F32 && cache_dtype == PKV_DTYPE_F32) ||
+                         (q_dtype == PKV_DTYPE_BF16 && cache_dtype == PKV_DTYPE_BF16) ||
+                         (q_dtype == PKV_DTYPE_BF16 && cache_dtype == PKV_DTYPE_FP8_E4M3);
+    if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == PKV_DTYPE_FP8_E4M3;
+    if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return PKV_ERR_INVALID_ARG;
+    if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(workspace, 16))
+        return PKV_ERR_ALIGNMENT;
+
+    const int64_t mp = max_parts(max_blocks_per_seq, partition_size);
+    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                                        block_size, partition_size);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    if (mp > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+
+    pkv::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    const size_t slots = size_t(num_seqs) * size_t(num_heads) * size_t(mp);
+    float* ws = static_cast<float*>(workspace);
+    a.ws_acc = need ? ws : nullptr;
+    a.ws_m = need ? ws + slots * size_t(head_dim) : nullptr;
+    a.ws_l = need ? ws + slots * size_t(head_dim + 1) : nullptr;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.part_blocks = part_tokens(partition_size) / pkv::kBlockTokens;
+    a.max_parts = int32_t(mp);
+    const float log2e = 1.4426950408889634f;
+    a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    const hipError_t e = pkv::launch_decode(cache_dtype, head_dim, num_heads / num_kv_heads, a,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// KV cache write through slot_mapping (gfx950).
+//
+// Source: bytelighting wiki "vLLM", 核心机制 / 工作原理, "Flattened 布局与
+// slot_mapping" -- every new token's logical position is sent to a physical
+// slot of the flattened block pool; ipipp.com vLLM article §二 -- blocks hold
+// 16 tokens.  Slot sl is offset sl % 16 of physical block sl / 16 in a pool
+// laid out [block][kv_head][16][head_dim].
+//
+// One thread moves one 16-byte chunk of the destination row: consecutive
+// threads cover consecutive bytes of a (token, head) row and then consecutive
+// heads, so both the reads of the new tokens and the writes into a block tile
+// are fully coalesced 16-byte accesses.  The fp8 variant reads 16 input
+// elements (32 or 64 bytes) per thread and quantises them with a bit-exact
+// round-to-nearest-even, saturating E4M3 encoder.
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+// OCP E4M3 encode of an fp32 value (already divided by the pool scale).
+// Integer formulation: normal results keep the top three mantissa bits with
+// round-to-nearest-even on the fp32 bit pattern; results below 2^-6 are the
+// round-to-nearest-even integer value of |y| * 2^9 (codes 0..8).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;    // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;   // |y| >= 448 or inf: saturate
+    const int e = int(a >> 23);                  // biased binary32 exponent
+    if (e >= 121) {                              // |y| >= 2^-6: normal E4M3
+        const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+        return sign | (r - (120u << 3));         // rebias 127 -> 7
+    }
+    if (e < 117) return sign;                    // |y| < 2^-10: rounds to zero
+    const uint32_t mant = (a & 0x7fffffu) | 0x800000u;
+    const int sh = 141 - e;                      // |y| * 2^9 = mant * 2^-sh, sh in [21, 24]
+    uint32_t q = mant >> sh;
+    const uint32_t rem = mant & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1);
+    q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    return sign | q;
+}
+
+template <int IN>
+__device__ __forceinline__ float load_elem(const uint8_t* p, int i) {
+    if constexpr (IN == kF32) {
+        return reinterpret_cast<const float*>(p)[i];
+    } else {
+        const uint32_t b = reinterpret_cast<const uint16_t*>(p)[i];
+        return __uint_as_float(b << 16);
+    }
+}
+
+// Copy: one 16-byte chunk per thread.  ROW = bytes per (token, head) row.
+template <int ROW>
+__global__ __launch_bounds__(256) void kv_copy_kernel(const uint8_t* __restrict__ k_new,
+                                                      const uint8_t* __restrict__ v_new,
+                                                      uint8_t* __restrict__ k_cache,
+                                                      uint8_t* __restrict__ v_cache,
+                                                      const int32_t* __restrict__ slots,
+                                                      int64_t total_chunks, int num_kv_heads, int num_slots) {
+    constexpr int CH = ROW / 16;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= total_chunks) return;
+    const int c = int(idx % CH);
+    const int64_t th = idx / CH;                 // token * heads + head
+    const int h = int(th % num_kv_heads);
+    const int64_t tok = th / num_kv_heads;
+    const int sl = slots[tok];
+    if (sl < 0 || sl >= num_slots) return;
+    const int64_t dst = ((int64_t(sl >> 4) * num_kv_heads + h) * kBlockTokens + (sl & 15)) * ROW + c * 16;
+    const int64_t src = th * ROW + c * 16;
+    const uint4 kx = *reinterpret_cast<const uint4*>(k_new + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(v_new + src);
+    *reinterpret_cast<uint4*>(k_cache + dst) = kx;
+    *reinterpret_cast<uint4*>(v_cache + dst) = vx;
+}
+
+// Quantise: 16 output codes (one 16-byte chunk) per thread.  D = head_dim.
+template <int IN, int D>
+__global__ __launch_bounds__(256) void kv_quant_kernel(const uint8_t* __restrict__ k_new,
+                                                       const uint8_t* __restrict__ v_new,
+                                                       uint8_t* __restrict__ k_cache,
+                                                       uint8_t* __restrict__ v_cache,
+                                                       const int32_t* __restrict__ slots,
+                                                       int64_t total_chunks, int num_kv_heads, int num_slots,
+                                                       float k_scale, float v_scale) {
+    constexpr int CH = D / 16;
+    constexpr int IN_ROW = D * (IN == kF32 ? 4 : 2);
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= total_chunks) return;
+    const int c = int(idx % CH);
+    const int64_t th = idx / CH;
+    const int h = int(th % num_kv_heads);
+    const int64_t tok = th / num_kv_heads;
+    const int sl = slots[tok];
+    if (sl < 0 || sl >= num_slots) return;
+    const int64_t dst = ((int64_t(sl >> 4) * num_kv_heads + h) * kBlockTokens + (sl & 15)) * D + c * 16;
+    const uint8_t* ks = k_new + th * IN_ROW + c * 16 * (IN == kF32 ? 4 : 2);
+    const uint8_t* vs = v_new + th * IN_ROW + c * 16 * (IN == kF32 ? 4 : 2);
+    uint32_t kw[4], vw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t kb = 0, vb = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kb |= e4m3_encode(load_elem<IN>(ks, w * 4 + e) / k_scale) << (8 * e);
+            vb |= e4m3_encode(load_elem<IN>(vs, w * 4 + e) / v_scale) << (8 * e);
+        }
+        kw[w] = kb;
+        vw[w] = vb;
+    }
+    *reinterpret_cast<uint4*>(k_cache + dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    *reinterpret_cast<uint4*>(v_cache + dst) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+}
+
+inline unsigned grid_for(int64_t n) { return unsigned((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const WriteArgs& a, hipStream_t stream) {
+    if (a.num_tokens == 0) return hipSuccess;
+    const auto* kn = static_cast<const uint8_t*>(a.k_new);
+    const auto* vn = static_cast<const uint8_t*>(a.v_new);
+    auto* kc = static_cast<uint8_t*>(a.k_cache);
+    auto* vc = static_cast<uint8_t*>(a.v_cache);
+    const int64_t rows = int64_t(a.num_tokens) * a.num_kv_heads;
+    if (in_dtype == cache_dtype) {
+        const int row = head_dim * dtype_bytes(cache_dtype);
+        const int64_t n = rows * (row / 16);
+        switch (row) {
+        case 64: kv_copy_kernel<64><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
+        case 128: kv_copy_kernel<128><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
+        case 256: kv_copy_kernel<256><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
+        case 512: kv_copy_kernel<512><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        const int64_t n = rows * (head_dim / 16);
+        const unsigned g = grid_for(n);
+#define PKV_QUANT(IN, D) kv_quant_kernel<IN, D><<<g, 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots, a.k_scale, a.v_scale)
+        if (in_dtype == kF32 && head_dim == 64) PKV_QUANT(kF32, 64);
+        else if (in_dtype == kF32 && head_dim == 128) PKV_QUANT(kF32, 128);
+        else if (in_dtype == kBF16 && head_dim == 64) PKV_QUANT(kBF16, 64);
+        else if (in_dtype == kBF16 && head_dim == 128) PKV_QUANT(kBF16, 128);
+        else return hipErrorInvalidValue;
+#undef PKV_QUANT
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

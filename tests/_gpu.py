@@ -1,0 +1,113 @@
+"""Helpers for the GPU parity tests: build the same cache on both sides.
+
+The GPU side builds its pools with the library's own write kernel; the oracle
+side builds numpy pools with the oracle's write.  Both start from the same
+generator output (tests never feed one side's results to the other, except
+that the GPU decode tests read GPU-written pools, which the write tests prove
+byte-identical to the oracle's).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_369_amd as pkv
+from paged_kv_cache_369_amd import workloads as W
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
+NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+
+
+def note(msg: str) -> None:
+    """Name the case on stdout before a GPU step (so a failure report says what ran)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        t = torch.from_numpy(a.astype(np.float32, copy=False))
+    elif dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "fp8":
+        t = torch.from_numpy(a.astype(np.uint8, copy=False))
+    elif dtype == "i32":
+        t = torch.from_numpy(a.astype(np.int32, copy=False))
+    else:
+        raise ValueError(dtype)
+    return t.cuda()
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Host copy of a GPU output as float64 (bf16 bits widened exactly)."""
+    if dtype == "bf16":
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def pool_shape(w: W.Workload, layout: W.Layout):
+    return (layout.num_blocks, w.num_kv_heads, W.BLOCK_SIZE, w.head_dim)
+
+
+def oracle_pools(w: W.Workload, layout: W.Layout, with_new=True):
+    shp = pool_shape(w, layout)
+    kp = np.full(shp, POISON[w.cache_dtype], dtype=NP[w.cache_dtype])
+    vp = kp.copy()
+    for b in layout.history:
+        oracle.kv_write(b.k, b.v, w.in_dtype, kp, vp, w.cache_dtype, b.slots, k_scale=w.k_scale, v_scale=w.v_scale)
+    if with_new:
+        oracle.kv_write(w.new_k, w.new_v, w.in_dtype, kp, vp, w.cache_dtype, layout.new_slots,
+                        k_scale=w.k_scale, v_scale=w.v_scale)
+    return kp, vp
+
+
+def gpu_pools(w: W.Workload, layout: W.Layout, with_new=True, poison=True):
+    shp = pool_shape(w, layout)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
+    kp = torch.empty(shp, dtype=tdt, device="cuda")
+    vp = torch.empty(shp, dtype=tdt, device="cuda")
+    if poison:
+        if w.cache_dtype == "fp8":
+            kp.fill_(0x7F); vp.fill_(0x7F)
+        else:
+            kp.fill_(float("nan")); vp.fill_(float("nan"))
+    else:
+        kp.zero_(); vp.zero_()
+    for b in layout.history:
+        pkv.paged_kv_write(to_dev(b.k, w.in_dtype), to_dev(b.v, w.in_dtype), kp, vp, to_dev(b.slots, "i32"),
+                           w.k_scale, w.v_scale)
+    if with_new:
+        pkv.paged_kv_write(to_dev(w.new_k, w.in_dtype), to_dev(w.new_v, w.in_dtype), kp, vp,
+                           to_dev(layout.new_slots, "i32"), w.k_scale, w.v_scale)
+    return kp, vp
+
+
+def gpu_decode(w: W.Workload, layout: W.Layout, kp, vp, partition_size=None, q=None):
+    q_dev = to_dev(w.q if q is None else q, w.q_dtype)
+    out = torch.empty_like(q_dev)
+    part = w.partition_size if partition_size is None else partition_size
+    pkv.paged_attention_decode(out, q_dev, kp, vp, to_dev(layout.block_table, "i32"),
+                               to_dev(w.context_lens, "i32"), w.scale, w.k_scale, w.v_scale, partition_size=part)
+    torch.cuda.synchronize()
+    return widen(to_host(out, w.q_dtype), w.q_dtype)
+
+
+def oracle_decode(w: W.Workload, layout: W.Layout, kp, vp, q=None):
+    return oracle.paged_attention(w.q if q is None else q, w.q_dtype, kp, vp, w.cache_dtype, layout.block_table,
+                                  w.context_lens, w.scale, w.k_scale, w.v_scale)
+
+
+def max_err(a: np.ndarray, b: np.ndarray):
+    d = np.abs(a - b)
+    i = int(np.argmax(d)) if d.size else 0
+    return (float(d.reshape(-1)[i]) if d.size else 0.0), np.unravel_index(i, d.shape) if d.size else None
