@@ -79,6 +79,33 @@ def cpu_baseline(w, host_pools, n_seqs, threads=0):
     return out, dt, oracle.num_threads(threads)
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch, steps: int) -> int:
+    """A plain device-to-device copy of COPY_BYTES per launch.
+
+    Reads and writes exactly COPY_BYTES each; rocprofv3's FETCH_SIZE and
+    WRITE_SIZE for this launch give the scale between those counters and
+    true HBM bytes on this machine.
+    """
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"copy_bytes": COPY_BYTES, "avg_us": us, "copy_GBps_read_plus_write": 2 * COPY_BYTES / us / 1e3}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +115,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's setting")
     ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the decode step, run a plain device copy of known size (HBM counter scale)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -102,6 +131,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration(torch, args.steps)
 
     t0 = time.perf_counter()
     w = W.make(args.workload, args.seed)

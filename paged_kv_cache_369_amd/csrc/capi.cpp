@@ -153,6 +153,7 @@ int paged_attention_decode(void* out,
     a.num_blocks = num_blocks;
     a.part_blocks = part_tokens(partition_size) / pkv::kBlockTokens;
     a.max_parts = int32_t(mp);
+    a.splits = 0;  // chosen by the launcher
     const float log2e = 1.4426950408889634f;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? v_scale : 1.0f;

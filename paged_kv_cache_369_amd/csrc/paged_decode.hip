@@ -10,11 +10,18 @@
 // whose partial softmax states are merged with the online-softmax rule
 // (bytelighting wiki "vLLM", 参考来源 names online softmax).
 //
-// Work decomposition: one workgroup (4 wave64s) per (partition p, group of G
-// query heads sharing one KV head, sequence s).  All G heads are served from
-// one read of each K/V tile, so every KV byte is fetched from HBM once.  Inside
-// a partition the waves take logical blocks round-robin, in chunks of up to 8
-// blocks per wave.  Per chunk a wave
+// Work decomposition: one workgroup (4 wave64s) per (group of G query heads
+// sharing one KV head, sequence s, split z).  All G heads are served from one
+// read of each K/V tile, so every KV byte is fetched from HBM once.  The
+// context is cut into partitions of part_blocks blocks; split z takes
+// partitions z, z + splits, z + 2*splits, ... and carries one online-softmax
+// state across them.  The head group is the fastest grid dimension, so the
+// round-robin placement of workgroups over the eight XCDs gives every XCD the
+// same share of KV heads (and the same share of the work); splits are the
+// slowest dimension, so the workgroups of splits a short sequence does not
+// need come last and exit at once.  Inside a partition the waves take
+// logical blocks round-robin, in chunks of up to 8 blocks per wave.  Per
+// chunk a wave
 //   1. streams its K tiles through a software pipeline (the next tile's
 //      16-byte loads are in flight while the current one is consumed; 4 lanes
 //      per token, each holding a quarter of the row) and forms G scores per
@@ -27,9 +34,10 @@
 //      slice of head_dim) and accumulates weight * value in fp32.
 // The block ids of a chunk are fetched with one vector load and read back
 // with v_readlane, so the loads of a tile never wait on a table read.  The
-// four waves' (max, sum, accumulator) states are merged through LDS; a
-// single-partition sequence writes its output directly, otherwise the
-// partition's state goes to the workspace and paged_reduce_kernel merges.
+// four waves' (max, sum, accumulator) states are merged through LDS; when a
+// sequence needs a single split the workgroup writes the output directly,
+// otherwise its state goes to the workspace and paged_reduce_kernel merges
+// the splits.
 //
 // Scores are kept in base-2 units (scale * k_scale * log2 e folded into one
 // factor).  Masking of the partial last block selects -inf scores and zero
@@ -132,9 +140,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
     using VT = typename std::conditional<S::VB == 16, uint4, uint2>::type;
     __shared__ float lds[NW][Lds<KV, D, G>::REGION];
 
-    const int p = blockIdx.x;
-    const int hg = blockIdx.y;
-    const int s = blockIdx.z;
+    const int hg = blockIdx.x;
+    const int s = blockIdx.y;
+    const int z = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int head0 = hg * G;
@@ -146,16 +154,14 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
     const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
 
     if (L == 0) {  // empty context: the output row is zero
-        if (p == 0) {
+        if (z == 0) {
             for (int i = threadIdx.x; i < G * D; i += NW * 64)
                 store_out<QT>(a.out, (int64_t(s) * a.num_heads + head0) * D + i, 0.0f);
         }
         return;
     }
-    if (p >= nparts) return;
+    if (z >= nparts) return;
 
-    const int b0 = p * a.part_blocks;
-    const int b1 = min(nblk, b0 + a.part_blocks);
     const int32_t* bt_row = a.block_table + int64_t(s) * a.max_blocks;
     const int64_t block_stride = int64_t(a.num_kv_heads) * S::TILE;
     const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + int64_t(kvh) * S::TILE;
@@ -203,6 +209,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
     const int vrow = lane / S::LPR;                 // V mapping row within a load
     const int vcol = (lane % S::LPR) * S::VB;       // byte offset within the row
 
+    for (int p = z; p < nparts; p += a.splits) {
+    const int b0 = p * a.part_blocks;
+    const int b1 = min(nblk, b0 + a.part_blocks);
     for (int c0 = b0; c0 < b1; c0 += NW * CB) {
         // blocks of this wave in this chunk: j = first + b * NW, b < nb
         const int first = c0 + wave;
@@ -374,6 +383,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
         if (b < nb) accum_block(va, b);
         wave_lds_sync();
     }
+    }
 
     // ---- wave-level reductions ----
 #pragma unroll
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
     __syncthreads();
 
     // ---- merge the waves and emit ----
-    const bool single = (nparts == 1);
+    const bool single = (nparts == 1 || a.splits == 1);
     for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
         const int h = idx / D;
         const int d = idx % D;
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
         if (single) {
             store_out<QT>(a.out, (int64_t(s) * a.num_heads + head) * D + d, (num / den) * a.v_scale);
         } else {
-            const int64_t slot = (int64_t(s) * a.num_heads + head) * a.max_parts + p;
+            const int64_t slot = (int64_t(s) * a.num_heads + head) * a.max_parts + z;
             a.ws_acc[slot * D + d] = num;
             if (d == 0) {
                 a.ws_m[slot] = M;
@@ -435,20 +445,24 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeArgs a) {
     }
 }
 
-// Merge the partitions of each (sequence, head): M = max m_p,
+// Merge the splits of each (sequence, head): M = max m_p,
 // out = v_scale * sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// One wave per (head, sequence); partition weights go through LDS.
+// One wave per (head, sequence); split weights go through LDS.  Grid x walks
+// the heads in the order (head % G, head / G) so that, like the decode grid,
+// consecutive workgroups (and hence XCDs) follow the KV-head group, and the
+// partial states are read on the XCD that wrote them.
 template <int QT, int D>
-__global__ __launch_bounds__(64) void paged_reduce_kernel(DecodeArgs a) {
-    constexpr int MAXP = 256;   // partitions merged per pass
+__global__ __launch_bounds__(64) void paged_reduce_kernel(DecodeArgs a, int G) {
+    constexpr int MAXP = 256;   // splits merged per pass
     constexpr int DPL = D / 64; // dims per lane
     __shared__ float wgt[MAXP];
-    const int head = blockIdx.x;
+    const int ngroups = a.num_heads / G;
+    const int head = (blockIdx.x % ngroups) * G + blockIdx.x / ngroups;
     const int s = blockIdx.y;
     const int lane = threadIdx.x;
     const int L = clamped_len(a, s);
     const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    const int nparts = min((nblk + a.part_blocks - 1) / a.part_blocks, a.splits);
     if (nparts <= 1) return;
     const int64_t base = (int64_t(s) * a.num_heads + head) * a.max_parts;
     float M = kNegInf;
@@ -486,11 +500,11 @@ __global__ __launch_bounds__(64) void paged_reduce_kernel(DecodeArgs a) {
 template <int KV, int D, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
-    dim3 grid(a.max_parts, a.num_heads / G, a.num_seqs);
+    dim3 grid(a.num_heads / G, a.num_seqs, a.splits);
     paged_decode_kernel<KV, D, G><<<grid, NW * 64, 0, stream>>>(a);
-    if (a.max_parts > 1) {
+    if (a.splits > 1) {
         dim3 rgrid(a.num_heads, a.num_seqs);
-        paged_reduce_kernel<QT, D><<<rgrid, 64, 0, stream>>>(a);
+        paged_reduce_kernel<QT, D><<<rgrid, 64, 0, stream>>>(a, G);
     }
     return hipGetLastError();
 }
@@ -517,9 +531,22 @@ static int heads_per_workgroup(int cache_dtype, int head_dim, int group) {
     return 1;
 }
 
-hipError_t launch_decode(int cache_dtype, int head_dim, int group, const DecodeArgs& a, hipStream_t stream) {
-    if (a.num_seqs == 0) return hipSuccess;
+// Splits per (sequence, head group): enough workgroups to fill the chip
+// several times over (about 8192), at least 4 so that one long sequence
+// cannot hold the whole launch, and never more than the partitions a row of
+// the block table can hold.
+static int splits_for(int num_seqs, int num_groups, int max_parts) {
+    const int64_t pairs = int64_t(num_seqs) * num_groups;
+    int64_t z = (8192 + pairs - 1) / pairs;
+    z = z < 4 ? 4 : z;
+    return int(z < max_parts ? z : max_parts);
+}
+
+hipError_t launch_decode(int cache_dtype, int head_dim, int group, const DecodeArgs& args, hipStream_t stream) {
+    if (args.num_seqs == 0) return hipSuccess;
     const int g = heads_per_workgroup(cache_dtype, head_dim, group);
+    DecodeArgs a = args;
+    if (a.splits <= 0) a.splits = splits_for(a.num_seqs, a.num_heads / g, a.max_parts);
     if (cache_dtype == kF32 && head_dim == 64) return launch_g<kF32, 64>(g, a, stream);
     if (cache_dtype == kF32 && head_dim == 128) return launch_g<kF32, 128>(g, a, stream);
     if (cache_dtype == kBF16 && head_dim == 64) return launch_g<kBF16, 64>(g, a, stream);

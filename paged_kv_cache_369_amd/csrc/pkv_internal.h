@@ -46,7 +46,8 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t num_blocks;
     int32_t part_blocks; // partition size in blocks
-    int32_t max_parts;   // ceil(max_blocks / part_blocks)
+    int32_t max_parts;   // ceil(max_blocks / part_blocks): workspace slots per (seq, head)
+    int32_t splits;      // workgroups per (seq, kv-head group), 1 <= splits <= max_parts
     float score_scale;   // scale * k_scale * log2(e): scores are kept in base-2 units
     float v_scale;       // 1 for f32 / bf16 pools
 };
