@@ -9,6 +9,11 @@ the pages are silent.
 Arrays are numpy.  Element types are named explicitly because numpy has no
 bfloat16 or fp8 type: ``"f32"`` (float32 array), ``"bf16"`` (uint16 array of
 bfloat16 bit patterns), ``"fp8"`` (uint8 array of OCP E4M3 codes).
+
+Pool layouts (see ``pkv_oracle.c``): the K pool is
+``[num_blocks, H_kv, D // X, block_size, X]`` with ``X = 16 // element size``
+(16-byte chunks of consecutive dimensions, chunk-major), the V pool is
+``[num_blocks, H_kv, D, block_size]`` (dimension-major).
 """
 from __future__ import annotations
 
@@ -24,6 +29,16 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 _NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+_ELT = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def k_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str, block_size: int = 16):
+    x = 16 // _ELT[dtype]
+    return (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+
+
+def v_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str = "", block_size: int = 16):
+    return (num_blocks, num_kv_heads, head_dim, block_size)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED = 0, 1, 2
 
@@ -114,17 +129,18 @@ def kv_write(k_new, v_new, in_dtype, k_cache, v_cache, cache_dtype, slot_mapping
              block_size=16, k_scale=1.0, v_scale=1.0):
     """Write tokens into the pools in place (see ``oracle_kv_write``).
 
-    k_new, v_new: [T, H_kv, D]; caches: [NB, H_kv, block_size, D]; slot_mapping: [T] int32.
+    k_new, v_new: [T, H_kv, D]; caches: ``k_pool_shape`` / ``v_pool_shape``; slot_mapping: [T] int32.
     """
     _check(k_new, in_dtype, "k_new"); _check(v_new, in_dtype, "v_new")
     _check(k_cache, cache_dtype, "k_cache"); _check(v_cache, cache_dtype, "v_cache")
     slot_mapping = np.ascontiguousarray(slot_mapping, dtype=np.int32)
     T, H, D = k_new.shape
-    if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape:
-        raise ValueError("shape mismatch")
     NB = k_cache.shape[0]
-    if k_cache.shape[1:] != (H, block_size, D) or slot_mapping.shape != (T,):
+    if v_new.shape != k_new.shape or slot_mapping.shape != (T,):
         raise ValueError("shape mismatch")
+    if k_cache.shape != k_pool_shape(NB, H, D, cache_dtype, block_size) or \
+            v_cache.shape != v_pool_shape(NB, H, D, cache_dtype, block_size):
+        raise ValueError("pool shape mismatch")
     st = _load().oracle_kv_write(_ptr(k_new), _ptr(v_new), DTYPES[in_dtype],
                                  _ptr(k_cache), _ptr(v_cache), DTYPES[cache_dtype],
                                  _ptr(slot_mapping), T, H, D, block_size, NB,
@@ -143,7 +159,8 @@ def paged_attention(q, q_dtype, k_cache, v_cache, cache_dtype, block_table, cont
     context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     B, Hq, D = q.shape
     NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    if k_cache.shape != (NB, Hkv, block_size, D) or v_cache.shape != k_cache.shape:
+    if k_cache.shape != k_pool_shape(NB, Hkv, D, cache_dtype, block_size) or \
+            v_cache.shape != v_pool_shape(NB, Hkv, D, cache_dtype, block_size):
         raise ValueError("cache shape mismatch")
     if block_table.ndim != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("table shape mismatch")

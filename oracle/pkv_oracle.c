@@ -29,9 +29,14 @@
  *
  * Conventions fixed where the pages are silent (each one is listed with its
  * reason in the repository's design notes):
- *  - Pool layout: separate K and V pools, each [num_blocks][num_kv_heads]
- *    [block_size][head_dim]; slot s lives at block s / block_size, offset
- *    s % block_size.
+ *  - Pool layout: separate K and V pools; slot s lives at block
+ *    s / block_size, offset s % block_size.  Within a (block, KV head) tile
+ *    the K pool stores each token row in 16-byte chunks of X = 16 / element
+ *    size consecutive dimensions, chunk-major:
+ *        K[block][kv_head][d / X][offset][d % X]
+ *    and the V pool stores the tile dimension-major:
+ *        V[block][kv_head][d][offset]
+ *    (head_dim must be a multiple of X).
  *  - Query head h reads KV head h / (num_heads / num_kv_heads).
  *  - A slot_mapping entry of -1 means "skip this token".
  *  - context_lens[s] counts every cached token of sequence s, including the
@@ -191,12 +196,30 @@ void oracle_bf16_to_double_n(const uint16_t* bits, double* out, int64_t n)
 /* KV cache write through slot_mapping                                       */
 /* ------------------------------------------------------------------------ */
 
-/* Offset, in elements, of (block, head, offset-in-block, dim) in a pool. */
-static size_t pool_index(int64_t block, int head, int off, int d,
-                         int num_kv_heads, int block_size, int head_dim)
+/* Elements per 16-byte K chunk for a pool element type. */
+static int k_chunk_elems(int dtype)
 {
-    return (((size_t)block * (size_t)num_kv_heads + (size_t)head) * (size_t)block_size
-            + (size_t)off) * (size_t)head_dim + (size_t)d;
+    size_t e = elt_size(dtype);
+    return e ? (int)(16 / e) : 0;
+}
+
+/* Offset, in elements, of (block, head, offset-in-block, dim) in the K pool:
+ * K[block][head][dim / X][offset][dim % X]. */
+static size_t k_index(int64_t block, int head, int off, int d,
+                      int num_kv_heads, int block_size, int head_dim, int X)
+{
+    size_t chunk = ((size_t)block * (size_t)num_kv_heads + (size_t)head) * (size_t)(head_dim / X)
+                   + (size_t)(d / X);
+    return (chunk * (size_t)block_size + (size_t)off) * (size_t)X + (size_t)(d % X);
+}
+
+/* Offset, in elements, of (block, head, offset-in-block, dim) in the V pool:
+ * V[block][head][dim][offset]. */
+static size_t v_index(int64_t block, int head, int off, int d,
+                      int num_kv_heads, int block_size, int head_dim)
+{
+    return (((size_t)block * (size_t)num_kv_heads + (size_t)head) * (size_t)head_dim + (size_t)d)
+           * (size_t)block_size + (size_t)off;
 }
 
 /*
@@ -229,6 +252,8 @@ int oracle_kv_write(const void* k_new, const void* v_new, int in_dtype,
         return ORC_ERR_UNSUPPORTED;
     if (quant && !(isfinite(k_scale) && k_scale > 0.0f && isfinite(v_scale) && v_scale > 0.0f))
         return ORC_ERR_INVALID_ARG;
+    if (head_dim % k_chunk_elems(cache_dtype) != 0)
+        return ORC_ERR_UNSUPPORTED;
 
     num_slots = (int64_t)num_blocks * block_size;
     seen = (uint8_t*)calloc((size_t)(num_slots > 0 ? num_slots : 1), 1);
@@ -257,14 +282,16 @@ int oracle_kv_write(const void* k_new, const void* v_new, int in_dtype,
         for (int h = 0; h < num_kv_heads; ++h) {
             for (int d = 0; d < head_dim; ++d) {
                 size_t src = ((size_t)i * num_kv_heads + h) * (size_t)head_dim + d;
-                size_t dst = pool_index(block, h, off, d, num_kv_heads, block_size, head_dim);
+                size_t kd = k_index(block, h, off, d, num_kv_heads, block_size, head_dim,
+                                    k_chunk_elems(cache_dtype));
+                size_t vd = v_index(block, h, off, d, num_kv_heads, block_size, head_dim);
                 if (!quant) {
                     size_t es = elt_size(cache_dtype);
-                    memcpy((char*)k_cache + dst * es, (const char*)k_new + src * es, es);
-                    memcpy((char*)v_cache + dst * es, (const char*)v_new + src * es, es);
+                    memcpy((char*)k_cache + kd * es, (const char*)k_new + src * es, es);
+                    memcpy((char*)v_cache + vd * es, (const char*)v_new + src * es, es);
                 } else {
-                    ((uint8_t*)k_cache)[dst] = quantise(load_as_float(k_new, in_dtype, src), k_scale);
-                    ((uint8_t*)v_cache)[dst] = quantise(load_as_float(v_new, in_dtype, src), v_scale);
+                    ((uint8_t*)k_cache)[kd] = quantise(load_as_float(k_new, in_dtype, src), k_scale);
+                    ((uint8_t*)v_cache)[vd] = quantise(load_as_float(v_new, in_dtype, src), v_scale);
                 }
             }
         }
@@ -293,15 +320,17 @@ typedef struct {
     pthread_mutex_t lock;
 } attn_job;
 
-/* Dequantised K or V element of logical token t of sequence s, KV head g. */
-static double kv_at(const attn_job* J, const void* pool, double pool_scale,
-                    int s, int g, int t, int d)
+/* Dequantised K (is_v = 0) or V (is_v = 1) element of logical token t of
+ * sequence s, KV head g, dimension d. */
+static double kv_at(const attn_job* J, int is_v, int s, int g, int t, int d)
 {
     int32_t block = J->block_table[(size_t)s * J->max_blocks_per_seq + t / J->block_size];
     int off = t % J->block_size;
-    size_t idx = pool_index(block, g, off, d, J->num_kv_heads, J->block_size, J->head_dim);
-    double x = load_as_double(pool, J->cache_dtype, idx);
-    return J->cache_dtype == ORC_FP8_E4M3 ? x * pool_scale : x;
+    size_t idx = is_v ? v_index(block, g, off, d, J->num_kv_heads, J->block_size, J->head_dim)
+                      : k_index(block, g, off, d, J->num_kv_heads, J->block_size, J->head_dim,
+                                k_chunk_elems(J->cache_dtype));
+    double x = load_as_double(is_v ? J->v_cache : J->k_cache, J->cache_dtype, idx);
+    return J->cache_dtype == ORC_FP8_E4M3 ? x * (is_v ? J->v_scale : J->k_scale) : x;
 }
 
 /* Score of query (s, h) against logical token t: scale * q . k_t */
@@ -310,7 +339,7 @@ static double score_at(const attn_job* J, int s, int h, int g, int t)
     double acc = 0.0;
     size_t qbase = ((size_t)s * J->num_heads + h) * (size_t)J->head_dim;
     for (int d = 0; d < J->head_dim; ++d)
-        acc += load_as_double(J->q, J->q_dtype, qbase + d) * kv_at(J, J->k_cache, J->k_scale, s, g, t, d);
+        acc += load_as_double(J->q, J->q_dtype, qbase + d) * kv_at(J, 0, s, g, t, d);
     return J->scale * acc;
 }
 
@@ -342,7 +371,7 @@ static void attend_one(const attn_job* J, int s, int h, double* row)
     for (int t = 0; t < L; ++t) {
         double p = w[t] / Z;
         for (int d = 0; d < J->head_dim; ++d)
-            row[d] += p * kv_at(J, J->v_cache, J->v_scale, s, g, t, d);
+            row[d] += p * kv_at(J, 1, s, g, t, d);
     }
     free(w);
 }
@@ -381,7 +410,7 @@ static void attend_one_split(const attn_job* J, int s, int h, double* row)
             double w = exp(score_at(J, s, h, g, t) - mp[p]);
             lp[p] += w;
             for (int d = 0; d < J->head_dim; ++d)
-                accp[(size_t)p * J->head_dim + d] += w * kv_at(J, J->v_cache, J->v_scale, s, g, t, d);
+                accp[(size_t)p * J->head_dim + d] += w * kv_at(J, 1, s, g, t, d);
         }
         if (mp[p] > M)
             M = mp[p];
@@ -459,6 +488,8 @@ int oracle_paged_attention(double* out, const void* q, int q_dtype,
     if (num_heads % num_kv_heads != 0)
         return ORC_ERR_INVALID_ARG;
     if (!(q_dtype == ORC_F32 || q_dtype == ORC_BF16) || elt_size(cache_dtype) == 0)
+        return ORC_ERR_UNSUPPORTED;
+    if (head_dim % k_chunk_elems(cache_dtype) != 0)
         return ORC_ERR_UNSUPPORTED;
     for (int s = 0; s < num_seqs; ++s) {
         int64_t L = context_lens[s];

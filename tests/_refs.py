@@ -10,15 +10,43 @@ import torch
 BS = 16
 
 
+def chunk_elems(dtype) -> int:
+    """Elements of one 16-byte K chunk for a numpy element type."""
+    return 16 // np.dtype(dtype).itemsize
+
+
+def empty_pools(num_blocks, hkv, d, fill, dtype):
+    """K pool [NB, H, D/X, 16, X] and V pool [NB, H, D, 16] filled with `fill`."""
+    x = chunk_elems(dtype)
+    kp = np.full((num_blocks, hkv, d // x, BS, x), fill, dtype=dtype)
+    vp = np.full((num_blocks, hkv, d, BS), fill, dtype=dtype)
+    return kp, vp
+
+
+def k_rows(kp, block, offs):
+    """K rows [H, n, D] of physical block `block` at offsets `offs`, by reshaping the chunked tile."""
+    tile = kp[block]                      # [H, D/X, 16, X]
+    h, nc, _, x = tile.shape
+    return np.transpose(tile[:, :, offs, :], (0, 2, 1, 3)).reshape(h, -1, nc * x)
+
+
+def v_rows(vp, block, offs):
+    """V rows [H, n, D] of physical block `block` at offsets `offs` (the tile is dimension-major)."""
+    return np.transpose(vp[block][:, :, offs], (0, 2, 1))
+
+
 def place_dense(dense_k, dense_v, lens, perm_blocks, num_blocks, hkv, d, fill=np.nan, dtype=np.float64):
-    """Build pools [NB, H, 16, D] and a block table from dense per-sequence [L, H, D] arrays.
+    """Build pools and a block table from dense per-sequence [L, H, D] arrays.
 
     Logical block j of sequence s goes to physical block perm_blocks[s][j]; the
-    block's 16 rows are the dense rows 16j..16j+15 (zero-padded past L), moved
-    into [H, 16, D] order by a transpose.
+    block's 16 rows are the dense rows 16j..16j+15 (padding past L keeps
+    `fill`).  The K tile [H, 16, D] is cut into 16-byte chunks of X
+    consecutive dimensions and stored chunk-major, [H, D/X, 16, X]; the V tile
+    is stored dimension-major, [H, D, 16] -- both by numpy reshapes and
+    transposes.
     """
-    kp = np.full((num_blocks, hkv, BS, d), fill, dtype=dtype)
-    vp = np.full((num_blocks, hkv, BS, d), fill, dtype=dtype)
+    kp, vp = empty_pools(num_blocks, hkv, d, fill, dtype)
+    x = chunk_elems(dtype)
     mb = max([len(p) for p in perm_blocks] + [1])
     bt = np.full((len(lens), mb), -1, dtype=np.int32)
     for s, L in enumerate(lens):
@@ -27,8 +55,9 @@ def place_dense(dense_k, dense_v, lens, perm_blocks, num_blocks, hkv, d, fill=np
         for j in range(nb):
             rows = slice(j * BS, min(L, (j + 1) * BS))
             n = rows.stop - rows.start
-            kp[perm_blocks[s][j], :, :n, :] = np.transpose(dense_k[s][rows], (1, 0, 2))
-            vp[perm_blocks[s][j], :, :n, :] = np.transpose(dense_v[s][rows], (1, 0, 2))
+            k = np.transpose(dense_k[s][rows], (1, 0, 2))           # [H, n, D]
+            kp[perm_blocks[s][j], :, :, :n, :] = np.transpose(k.reshape(hkv, n, d // x, x), (0, 2, 1, 3))
+            vp[perm_blocks[s][j], :, :, :n] = np.transpose(dense_v[s][rows], (1, 2, 0))  # [H, D, n]
     return kp, vp, bt
 
 
