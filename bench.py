@@ -183,7 +183,7 @@ def summarize_traffic(args) -> int:
     fetch = _per_kernel(args.dec_fetch, "FETCH_SIZE")
     write = _per_kernel(args.dec_write, "WRITE_SIZE")
     kernels = {}
-    for key in ("paged_decode_kernel", "paged_reduce_kernel"):
+    for key in ("paged_decode_kernel", "paged_fixup_kernel"):
         f_kib, w_kib = _pick(fetch, key), _pick(write, key)
         kernels[key] = {"fetch_kib": f_kib, "write_kib": w_kib,
                         "fetch_bytes": f_kib * 1024 * fscale, "write_bytes": w_kib * 1024 * wscale}
@@ -227,10 +227,10 @@ def summarize_traffic(args) -> int:
 def oracle_baseline(w, out_dev, q_dtype, max_seqs: int):
     """Time the CPU oracle (as it stands) on the first max_seqs sequences and compare every output."""
     import oracle  # test infrastructure, used only for this reported baseline and check
-    shp = (w.layout.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
     npd = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.cache_dtype]
-    kp = np.zeros(shp, dtype=npd)
-    vp = np.zeros(shp, dtype=npd)
+    nb, hkv, d = w.layout.num_blocks, w.num_kv_heads, w.head_dim
+    kp = np.zeros(oracle.k_pool_shape(nb, hkv, d, w.cache_dtype), dtype=npd)
+    vp = np.zeros(oracle.v_pool_shape(nb, hkv, d, w.cache_dtype), dtype=npd)
     for b in w.layout.history:
         oracle.kv_write(b.k, b.v, w.in_dtype, kp, vp, w.cache_dtype, b.slots, k_scale=w.k_scale, v_scale=w.v_scale)
     oracle.kv_write(w.new_k, w.new_v, w.in_dtype, kp, vp, w.cache_dtype, w.layout.new_slots,
@@ -256,7 +256,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa8b", choices=sorted(WORKLOAD_DESC))
-    ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's setting")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="-1 = the workload's setting (0 = balanced split only)")
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-oracle baseline and check (-1 = all, 0 = skip)")
     ap.add_argument("--seed", type=int, default=None)
@@ -301,9 +302,9 @@ def main() -> int:
 
     # device-resident inputs
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
-    shp = (layout.num_blocks, w.num_kv_heads, W.BLOCK_SIZE, w.head_dim)
-    kc = torch.zeros(shp, dtype=tdt, device="cuda")
-    vc = torch.zeros(shp, dtype=tdt, device="cuda")
+    kc = torch.zeros(pkv.k_cache_shape(layout.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype),
+                     dtype=tdt, device="cuda")
+    vc = torch.zeros(pkv.v_cache_shape(layout.num_blocks, w.num_kv_heads, w.head_dim), dtype=tdt, device="cuda")
     for b in layout.history:
         pkv.paged_kv_write(_dev(b.k, w.in_dtype, torch), _dev(b.v, w.in_dtype, torch), kc, vc,
                            _dev(b.slots, "i32", torch), w.k_scale, w.v_scale)
@@ -315,8 +316,8 @@ def main() -> int:
     out = torch.empty_like(q)
     bt = _dev(layout.block_table, "i32", torch)
     cl = _dev(w.context_lens, "i32", torch)
-    ws_bytes = pkv.paged_attention_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
-                                                   W.BLOCK_SIZE, part)
+    ws_bytes = pkv.paged_attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                                   w.max_blocks_per_seq, W.BLOCK_SIZE, part)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
@@ -376,12 +377,12 @@ def main() -> int:
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": W.BLOCK_SIZE, "kv_dtype": w.cache_dtype, "q_dtype": w.q_dtype,
                    "sum_context": int(w.context_lens.sum()),
-                   "partition_size": part or pkv.DEFAULT_PARTITION, "kv_bytes": kv_bytes},
+                   "partition_size": part, "kv_bytes": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "decode call: paged_decode_kernel + paged_reduce_kernel",
+                     "kernel": "decode call: paged_decode_kernel + paged_fixup_kernel",
                      "avg_us": dec_us,
                      "algorithmic_bytes_per_call": kv_bytes},
         "write_us": float(np.mean(t_write)),

@@ -33,9 +33,15 @@
  *    multiple of num_kv_heads.  Supported (q, cache) dtype pairs for decode:
  *    (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  *
- * Pool layout (K and V pools are separate and identical in shape):
- *    cache[num_blocks][num_kv_heads][block_size][head_dim]
- * Slot `sl` is offset sl % block_size of physical block sl / block_size.
+ * Pool layout.  K and V pools are separate, num_blocks * num_kv_heads tiles
+ * of block_size * head_dim elements each; slot `sl` is offset
+ * o = sl % block_size of physical block b = sl / block_size.  Inside a
+ * (block, KV head) tile (the pages fix no in-block layout; this one lets the
+ * decode kernel load matrix-core operands directly):
+ *    k_cache[b][kv_head][d / X][o][d % X]   X = 16 / element bytes
+ *            (each token row stored as 16-byte chunks of X consecutive
+ *             dimensions, chunk-major: X = 4 f32, 8 bf16, 16 fp8)
+ *    v_cache[b][kv_head][d][o]              (dimension-major)
  * fp8 pools hold OCP E4M3 codes (bias 7, max 448, no infinities); one fp32
  * scale per pool: value = decode(code) * k_scale (K) or * v_scale (V).
  */
@@ -64,7 +70,9 @@ typedef enum pkv_status {
     PKV_ERR_HIP = 5           /* the HIP runtime reported an error while launching */
 } pkv_status;
 
-/* Version of this ABI (incremented on any incompatible change). */
+/* Version of this ABI (incremented on any incompatible change; 2 = the
+ * chunked-K / dimension-major-V pool layout and the workspace query that
+ * takes num_kv_heads). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -78,7 +86,7 @@ const char* pkv_status_string(int status);
  *
  * k_new, v_new   [num_tokens][num_kv_heads][head_dim] in in_dtype.
  * k_cache,
- * v_cache        [num_blocks][num_kv_heads][block_size][head_dim] in cache_dtype.
+ * v_cache        pools in cache_dtype, layouts as above.
  * slot_mapping   [num_tokens] int32: slot of token i, or -1 to skip it.
  *                Slots must be distinct (a repeated slot gives an unspecified
  *                one of the written values).
@@ -102,13 +110,16 @@ int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
 
 /*
  * paged_attention_workspace_bytes -- bytes of device workspace that
- * paged_attention_decode needs for these sizes (host; 0 when every sequence
- * fits one partition, i.e. max_blocks_per_seq*block_size <= partition size).
- * partition_size as in paged_attention_decode (0 = the default).  Returns 0
- * for arguments paged_attention_decode would reject.
+ * paged_attention_decode needs for these sizes (host; no device call).  The
+ * workspace holds a small header and the partial softmax states of the runs
+ * (sequence, group of query heads sharing a KV head) that the balanced work
+ * split cuts between waves: two states per work range, 4096 ranges, or more
+ * when partition_size caps the blocks a range covers.
+ * partition_size as in paged_attention_decode.  Returns 0 for arguments
+ * paged_attention_decode would reject.
  */
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                       int32_t max_blocks_per_seq, int32_t block_size,
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t partition_size);
 
 /*
@@ -133,14 +144,19 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * scale          softmax scale (typically 1/sqrt(head_dim)).
  * k_scale,
  * v_scale        fp8 pool scales (ignored for F32/BF16 pools).
- * partition_size tokens per work unit along the context (split-K): 0 = the
- *                default (512), otherwise a positive multiple of 16.  When a
- *                sequence spans several partitions each writes a partial
- *                result to the workspace and a second kernel merges them.
+ * partition_size split-K granularity: 0 = balanced split only (the context
+ *                blocks of all runs are cut into as many equal work ranges
+ *                as the chip runs waves), otherwise a positive multiple of
+ *                16: no work range covers more than partition_size tokens
+ *                (more ranges are made).  A run cut between ranges has its
+ *                partial states merged by a second kernel.  The split
+ *                changes rounding only.
  * workspace      device buffer of >= paged_attention_workspace_bytes(...)
- *                bytes (may be NULL when that is 0), owned by the caller,
- *                contents need no initialisation.
- * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT,
+ *                bytes, owned by the caller, contents need no
+ *                initialisation; calls that share a workspace must be
+ *                ordered (same stream).
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (also when
+ * num_seqs * runs * max_blocks_per_seq >= 2^31), PKV_ERR_ALIGNMENT,
  * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  num_seqs == 0 is a no-op.
  */
 int paged_attention_decode(void* out,

@@ -11,10 +11,13 @@ raises.
     paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, scale, ...)
     paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, ...)
 
-Layouts: new tokens ``[T, H_kv, D]``; pools ``[num_blocks, H_kv, 16, D]``
-(fp8 pools as ``torch.uint8`` or ``torch.float8_e4m3fn``); ``q`` and ``out``
-``[B, H_q, D]``; ``block_table`` ``[B, max_blocks]`` int32 (-1 padded);
-``context_lens`` ``[B]`` int32; ``slot_mapping`` ``[T]`` int32 (-1 = skip).
+Layouts: new tokens ``[T, H_kv, D]``; K pool ``[num_blocks, H_kv, D // X,
+16, X]`` with ``X = 16 // element bytes`` (each token row as 16-byte chunks
+of consecutive dimensions, chunk-major), V pool ``[num_blocks, H_kv, D, 16]``
+(dimension-major) -- see ``k_cache_shape`` / ``v_cache_shape``; fp8 pools as
+``torch.uint8`` or ``torch.float8_e4m3fn``; ``q`` and ``out`` ``[B, H_q, D]``;
+``block_table`` ``[B, max_blocks]`` int32 (-1 padded); ``context_lens``
+``[B]`` int32; ``slot_mapping`` ``[T]`` int32 (-1 = skip).
 """
 from __future__ import annotations
 
@@ -22,10 +25,10 @@ import ctypes
 import os
 
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
-           "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "DEFAULT_PARTITION"]
+           "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
 BLOCK_SIZE = 16
-DEFAULT_PARTITION = 512
+_ELT = {"f32": 4, "bf16": 2, "fp8": 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 _lib = None
@@ -54,7 +57,7 @@ def _load():
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.paged_kv_write.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, i32, i32, i32, i32, f32, f32, p]
     lib.paged_kv_write.restype = ctypes.c_int
-    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_attention_workspace_bytes.restype = sz
     lib.paged_attention_decode.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p,
                                            i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
@@ -65,6 +68,30 @@ def _load():
 
 def pkv_abi_version() -> int:
     return _load().pkv_abi_version()
+
+
+def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+    """Shape of a K pool: [num_blocks, H_kv, D // X, 16, X], X = 16 // element bytes ("f32", "bf16", "fp8")."""
+    x = 16 // _ELT[dtype]
+    return (num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str = ""):
+    """Shape of a V pool: [num_blocks, H_kv, D, 16]."""
+    return (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE)
+
+
+def _pools(k_cache, v_cache):
+    """(num_blocks, H_kv, head_dim) of a K/V pool pair, checking both layouts."""
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("K pool must be [NB, H, D//X, 16, X] and V pool [NB, H, D, 16]")
+    NB, H, nc, BS, X = k_cache.shape
+    D = nc * X
+    if X * k_cache.element_size() != 16 or BS != BLOCK_SIZE:
+        raise ValueError("K pool chunks must be 16 bytes of 16-token blocks")
+    if tuple(v_cache.shape) != (NB, H, D, BLOCK_SIZE) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("V pool shape/dtype does not match the K pool")
+    return NB, H, D
 
 
 def _dtype_code(t) -> int:
@@ -102,22 +129,23 @@ def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float 
     """Store new tokens' K/V at their slots (copy, or quantise into an fp8 pool)."""
     lib = _load()
     T, H, D = k_new.shape
-    NB, Hc, BS, Dc = k_cache.shape
-    if (Hc, Dc) != (H, D) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+    NB, Hc, Dc = _pools(k_cache, v_cache)
+    if (Hc, Dc) != (H, D) or v_new.shape != k_new.shape:
         raise ValueError("shape mismatch between new tokens and pools")
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
     st = lib.paged_kv_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
                             _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
-                            _dev(slot_mapping, "slot_mapping"), T, H, D, BS, NB,
+                            _dev(slot_mapping, "slot_mapping"), T, H, D, BLOCK_SIZE, NB,
                             float(k_scale), float(v_scale), _stream(stream))
     _check(st, "paged_kv_write")
 
 
-def paged_attention_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_blocks_per_seq: int,
-                                    block_size: int = BLOCK_SIZE, partition_size: int = 0) -> int:
-    return int(_load().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
-                                                       block_size, partition_size))
+def paged_attention_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                    max_blocks_per_seq: int, block_size: int = BLOCK_SIZE,
+                                    partition_size: int = 0) -> int:
+    return int(_load().paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                       max_blocks_per_seq, block_size, partition_size))
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float,
@@ -127,13 +155,13 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
     import torch
     lib = _load()
     B, Hq, D = q.shape
-    NB, Hkv, BS, Dc = k_cache.shape
-    if out.shape != q.shape or Dc != D or v_cache.shape != k_cache.shape:
+    NB, Hkv, Dc = _pools(k_cache, v_cache)
+    if out.shape != q.shape or Dc != D:
         raise ValueError("shape mismatch")
     if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_table must be [B, max_blocks] and context_lens [B]")
     MB = block_table.shape[1]
-    need = paged_attention_workspace_bytes(B, Hq, D, MB, BS, partition_size)
+    need = paged_attention_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
@@ -141,6 +169,6 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
     st = lib.paged_attention_decode(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),
                                     _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
                                     _dev(block_table, "block_table"), MB, _dev(context_lens, "context_lens"),
-                                    B, Hq, Hkv, D, BS, NB, float(scale), float(k_scale), float(v_scale),
+                                    B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), float(k_scale), float(v_scale),
                                     int(partition_size), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "paged_attention_decode")

@@ -9,20 +9,25 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool known_dtype(int dt) { return dt == PKV_DTYPE_F32 || dt == PKV_DTYPE_BF16 || dt == PKV_DTYPE_FP8_E4M3; }
 
-int part_tokens(int32_t partition_size) { return partition_size == 0 ? pkv::kDefaultPartition : partition_size; }
-
-// Partitions per sequence row of the workspace, or -1 for a bad partition size.
-int64_t max_parts(int32_t max_blocks_per_seq, int32_t partition_size) {
+// Work ranges the decode may create for these sizes (the workspace holds two
+// partial-state slots per range): one per persistent wave, or more when a
+// partition size caps the blocks one range covers.  -1: invalid arguments.
+int64_t max_ranges(int32_t num_seqs, int32_t runs, int32_t max_blocks_per_seq, int32_t partition_size) {
     if (partition_size < 0 || (partition_size % pkv::kBlockTokens) != 0) return -1;
-    const int64_t pb = part_tokens(partition_size) / pkv::kBlockTokens;
-    const int64_t mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
-    return (mb + pb - 1) / pb;
+    int64_t n = pkv::kMaxWaves;
+    if (partition_size > 0) {
+        const int64_t pb = partition_size / pkv::kBlockTokens;
+        const int64_t units = int64_t(num_seqs) * runs * max_blocks_per_seq;
+        const int64_t need = (units + pb - 1) / pb;
+        n = need > n ? need : n;
+    }
+    return n;
 }
 
 }  // namespace
@@ -81,15 +86,16 @@ int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                       int32_t max_blocks_per_seq, int32_t block_size,
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq < 0 ||
-        block_size != pkv::kBlockTokens)
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        max_blocks_per_seq < 0 || block_size != pkv::kBlockTokens)
         return 0;
-    const int64_t mp = max_parts(max_blocks_per_seq, partition_size);
-    if (mp <= 1) return 0;
-    return size_t(num_seqs) * size_t(num_heads) * size_t(mp) * size_t(head_dim + 2) * sizeof(float);
+    const int rh = pkv::run_heads(num_heads / num_kv_heads);
+    const int64_t nr = max_ranges(num_seqs, num_heads / rh, max_blocks_per_seq, partition_size);
+    if (nr < 0) return 0;
+    return size_t(pkv::kWsHeader + 2 * nr * pkv::slot_floats(rh, head_dim)) * sizeof(float);
 }
 
 int paged_attention_decode(void* out,
@@ -120,7 +126,6 @@ int paged_attention_decode(void* out,
         return PKV_ERR_INVALID_ARG;
     if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
     if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
-    if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
         return PKV_ERR_INVALID_ARG;
@@ -128,11 +133,15 @@ int paged_attention_decode(void* out,
         !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(workspace, 16))
         return PKV_ERR_ALIGNMENT;
 
-    const int64_t mp = max_parts(max_blocks_per_seq, partition_size);
-    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
-                                                        block_size, partition_size);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-    if (mp > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+    const int rh = pkv::run_heads(num_heads / num_kv_heads);
+    const int runs = num_heads / rh;
+    if (int64_t(num_seqs) * runs * max_blocks_per_seq >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                        max_blocks_per_seq, block_size, partition_size);
+    if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    const int64_t slot = pkv::slot_floats(rh, head_dim);
+    int64_t cap = (int64_t(workspace_bytes / sizeof(float)) - pkv::kWsHeader) / (2 * slot);
+    cap = cap < 0x7fffffff ? cap : 0x7fffffff;
 
     pkv::DecodeArgs a;
     a.out = out;
@@ -141,24 +150,22 @@ int paged_attention_decode(void* out,
     a.v_cache = v_cache;
     a.block_table = block_table;
     a.context_lens = context_lens;
-    const size_t slots = size_t(num_seqs) * size_t(num_heads) * size_t(mp);
-    float* ws = static_cast<float*>(workspace);
-    a.ws_acc = need ? ws : nullptr;
-    a.ws_m = need ? ws + slots * size_t(head_dim) : nullptr;
-    a.ws_l = need ? ws + slots * size_t(head_dim + 1) : nullptr;
+    a.ws = static_cast<float*>(workspace);
     a.max_blocks = max_blocks_per_seq;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.num_blocks = num_blocks;
-    a.part_blocks = part_tokens(partition_size) / pkv::kBlockTokens;
-    a.max_parts = int32_t(mp);
-    a.splits = 0;  // chosen by the launcher
+    a.group = num_heads / num_kv_heads;
+    a.rh = rh;
+    a.runs = runs;
+    a.part_blocks = partition_size / pkv::kBlockTokens;
+    a.nwv_cap = int32_t(cap);
+    a.slot_floats = int32_t(slot);
     const float log2e = 1.4426950408889634f;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
-    const hipError_t e = pkv::launch_decode(cache_dtype, head_dim, num_heads / num_kv_heads, a,
-                                            static_cast<hipStream_t>(stream));
+    const hipError_t e = pkv::launch_decode(cache_dtype, head_dim, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -3,15 +3,19 @@
 // Source: bytelighting wiki "vLLM", 核心机制 / 工作原理, "Flattened 布局与
 // slot_mapping" -- every new token's logical position is sent to a physical
 // slot of the flattened block pool; ipipp.com vLLM article §二 -- blocks hold
-// 16 tokens.  Slot sl is offset sl % 16 of physical block sl / 16 in a pool
-// laid out [block][kv_head][16][head_dim].
+// 16 tokens.  Slot sl is offset sl % 16 of physical block sl / 16.  Inside a
+// (block, KV head) tile the K pool keeps each token row as 16-byte chunks of
+// consecutive dimensions, chunk-major ([d / X][offset][d % X], X = 16 bytes of
+// elements), and the V pool is dimension-major ([d][offset]) -- the layouts
+// the decode kernel's matrix-core operands load directly.
 //
-// One thread moves one 16-byte chunk of the destination row: consecutive
-// threads cover consecutive bytes of a (token, head) row and then consecutive
-// heads, so both the reads of the new tokens and the writes into a block tile
-// are fully coalesced 16-byte accesses.  The fp8 variant reads 16 input
-// elements (32 or 64 bytes) per thread and quantises them with a bit-exact
-// round-to-nearest-even, saturating E4M3 encoder.
+// One thread per 16-byte K chunk of a (token, head) row: consecutive threads
+// take consecutive chunks and then consecutive heads, so the reads of the new
+// tokens are fully coalesced and every K store is one aligned 16-byte write.
+// The same thread scatters the chunk's dimensions into the V tile (one element
+// per dimension row).  The fp8 variant reads 16 input elements per thread and
+// quantises them with a bit-exact round-to-nearest-even, saturating E4M3
+// encoder.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -52,15 +56,26 @@ __device__ __forceinline__ float load_elem(const uint8_t* p, int i) {
     }
 }
 
-// Copy: one 16-byte chunk per thread.  ROW = bytes per (token, head) row.
-template <int ROW>
+// Byte offset of the 16-byte K chunk `c` of (slot, head) and of V element
+// (slot, head, dim) for a tile of CH chunks / D dims of ELT-byte elements.
+__device__ __forceinline__ int64_t k_chunk_offset(int sl, int h, int c, int num_kv_heads, int CH) {
+    return ((int64_t(sl >> 4) * num_kv_heads + h) * CH + c) * (kBlockTokens * 16) + (sl & 15) * 16;
+}
+__device__ __forceinline__ int64_t v_elem_offset(int sl, int h, int d, int num_kv_heads, int D, int ELT) {
+    return ((int64_t(sl >> 4) * num_kv_heads + h) * D + d) * (kBlockTokens * ELT) + (sl & 15) * ELT;
+}
+
+// Copy (same dtype): one 16-byte chunk (X elements) per thread.  D = head_dim.
+template <int ELT, int D>
 __global__ __launch_bounds__(256) void kv_copy_kernel(const uint8_t* __restrict__ k_new,
                                                       const uint8_t* __restrict__ v_new,
                                                       uint8_t* __restrict__ k_cache,
                                                       uint8_t* __restrict__ v_cache,
                                                       const int32_t* __restrict__ slots,
                                                       int64_t total_chunks, int num_kv_heads, int num_slots) {
+    constexpr int ROW = D * ELT;
     constexpr int CH = ROW / 16;
+    constexpr int X = 16 / ELT;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= total_chunks) return;
     const int c = int(idx % CH);
@@ -69,15 +84,25 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(const uint8_t* __restrict_
     const int64_t tok = th / num_kv_heads;
     const int sl = slots[tok];
     if (sl < 0 || sl >= num_slots) return;
-    const int64_t dst = ((int64_t(sl >> 4) * num_kv_heads + h) * kBlockTokens + (sl & 15)) * ROW + c * 16;
     const int64_t src = th * ROW + c * 16;
     const uint4 kx = *reinterpret_cast<const uint4*>(k_new + src);
     const uint4 vx = *reinterpret_cast<const uint4*>(v_new + src);
-    *reinterpret_cast<uint4*>(k_cache + dst) = kx;
-    *reinterpret_cast<uint4*>(v_cache + dst) = vx;
+    *reinterpret_cast<uint4*>(k_cache + k_chunk_offset(sl, h, c, num_kv_heads, CH)) = kx;
+    const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+        const int64_t dst = v_elem_offset(sl, h, c * X + e, num_kv_heads, D, ELT);
+        if constexpr (ELT == 4) {
+            *reinterpret_cast<uint32_t*>(v_cache + dst) = w[e];
+        } else if constexpr (ELT == 2) {
+            *reinterpret_cast<uint16_t*>(v_cache + dst) = uint16_t(w[e / 2] >> (16 * (e % 2)));
+        } else {
+            v_cache[dst] = uint8_t(w[e / 4] >> (8 * (e % 4)));
+        }
+    }
 }
 
-// Quantise: 16 output codes (one 16-byte chunk) per thread.  D = head_dim.
+// Quantise: 16 output codes (one 16-byte K chunk) per thread.  D = head_dim.
 template <int IN, int D>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const uint8_t* __restrict__ k_new,
                                                        const uint8_t* __restrict__ v_new,
@@ -87,7 +112,8 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint8_t* __restrict
                                                        int64_t total_chunks, int num_kv_heads, int num_slots,
                                                        float k_scale, float v_scale) {
     constexpr int CH = D / 16;
-    constexpr int IN_ROW = D * (IN == kF32 ? 4 : 2);
+    constexpr int IN_ELT = IN == kF32 ? 4 : 2;
+    constexpr int IN_ROW = D * IN_ELT;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= total_chunks) return;
     const int c = int(idx % CH);
@@ -96,23 +122,20 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint8_t* __restrict
     const int64_t tok = th / num_kv_heads;
     const int sl = slots[tok];
     if (sl < 0 || sl >= num_slots) return;
-    const int64_t dst = ((int64_t(sl >> 4) * num_kv_heads + h) * kBlockTokens + (sl & 15)) * D + c * 16;
-    const uint8_t* ks = k_new + th * IN_ROW + c * 16 * (IN == kF32 ? 4 : 2);
-    const uint8_t* vs = v_new + th * IN_ROW + c * 16 * (IN == kF32 ? 4 : 2);
-    uint32_t kw[4], vw[4];
+    const uint8_t* ks = k_new + th * IN_ROW + c * 16 * IN_ELT;
+    const uint8_t* vs = v_new + th * IN_ROW + c * 16 * IN_ELT;
+    uint32_t kw[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        uint32_t kb = 0, vb = 0;
+        uint32_t kb = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kb |= e4m3_encode(load_elem<IN>(ks, w * 4 + e) / k_scale) << (8 * e);
-            vb |= e4m3_encode(load_elem<IN>(vs, w * 4 + e) / v_scale) << (8 * e);
-        }
+        for (int e = 0; e < 4; ++e) kb |= e4m3_encode(load_elem<IN>(ks, w * 4 + e) / k_scale) << (8 * e);
         kw[w] = kb;
-        vw[w] = vb;
     }
-    *reinterpret_cast<uint4*>(k_cache + dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    *reinterpret_cast<uint4*>(v_cache + dst) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+    *reinterpret_cast<uint4*>(k_cache + k_chunk_offset(sl, h, c, num_kv_heads, CH)) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        v_cache[v_elem_offset(sl, h, c * 16 + e, num_kv_heads, D, 1)] = uint8_t(e4m3_encode(load_elem<IN>(vs, e) / v_scale));
 }
 
 inline unsigned grid_for(int64_t n) { return unsigned((n + 255) / 256); }
@@ -127,15 +150,17 @@ hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const Wr
     auto* vc = static_cast<uint8_t*>(a.v_cache);
     const int64_t rows = int64_t(a.num_tokens) * a.num_kv_heads;
     if (in_dtype == cache_dtype) {
-        const int row = head_dim * dtype_bytes(cache_dtype);
-        const int64_t n = rows * (row / 16);
-        switch (row) {
-        case 64: kv_copy_kernel<64><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
-        case 128: kv_copy_kernel<128><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
-        case 256: kv_copy_kernel<256><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
-        case 512: kv_copy_kernel<512><<<grid_for(n), 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots); break;
-        default: return hipErrorInvalidValue;
-        }
+        const int64_t n = rows * (head_dim * dtype_bytes(cache_dtype) / 16);
+        const unsigned g = grid_for(n);
+#define PKV_COPY(ELT, D) kv_copy_kernel<ELT, D><<<g, 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots)
+        if (cache_dtype == kF32 && head_dim == 64) PKV_COPY(4, 64);
+        else if (cache_dtype == kF32 && head_dim == 128) PKV_COPY(4, 128);
+        else if (cache_dtype == kBF16 && head_dim == 64) PKV_COPY(2, 64);
+        else if (cache_dtype == kBF16 && head_dim == 128) PKV_COPY(2, 128);
+        else if (cache_dtype == kFP8 && head_dim == 64) PKV_COPY(1, 64);
+        else if (cache_dtype == kFP8 && head_dim == 128) PKV_COPY(1, 128);
+        else return hipErrorInvalidValue;
+#undef PKV_COPY
     } else {
         const int64_t n = rows * (head_dim / 16);
         const unsigned g = grid_for(n);

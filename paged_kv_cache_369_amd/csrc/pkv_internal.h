@@ -8,12 +8,19 @@
 
 namespace pkv {
 
-constexpr int kBlockTokens = 16;       // tokens per physical block
-constexpr int kDefaultPartition = 512; // tokens per split-K work unit
+constexpr int kBlockTokens = 16;  // tokens per physical block
+constexpr int kMaxRunHeads = 16;  // query heads one wave serves (matrix-core tile width)
+constexpr int kMaxWaves = 4096;   // persistent waves per launch (16 per CU on a 256-CU MI355X)
+
 
 enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : dt == kFP8 ? 1 : 0; }
+
+// Pool layouts (elements; X = 16 / element bytes):
+//   K[block][kv_head][d / X][offset][d % X]   (16-byte chunks of a token row, chunk-major)
+//   V[block][kv_head][d][offset]              (dimension-major)
+inline int k_chunk_elems(int dt) { return 16 / dtype_bytes(dt); }
 
 struct WriteArgs {
     const void* k_new;
@@ -30,6 +37,24 @@ struct WriteArgs {
 
 hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const WriteArgs& a, hipStream_t stream);
 
+// Query heads of one run: the largest divisor of the GQA group that is at
+// most kMaxRunHeads.  A run is (sequence, group of run_heads query heads that
+// share one KV head); each KV tile of the run is read once for all its heads.
+inline int run_heads(int group) {
+    for (int g = group < kMaxRunHeads ? group : kMaxRunHeads; g > 1; --g)
+        if (group % g == 0) return g;
+    return 1;
+}
+
+// Workspace: a 16-word header (word 0: total units, word 1: work ranges)
+// followed by two partial-state slots per work range.  Slot layout (floats):
+// 8 header words {seq, run, first block, end block, kind, -, -, -}, m[16],
+// l[16], acc[run_heads][D].
+constexpr int kWsHeader = 16;
+constexpr int kSlotHead = 8 + 2 * kMaxRunHeads;
+inline int64_t slot_floats(int rh, int head_dim) { return kSlotHead + int64_t(rh) * head_dim; }
+enum SlotKind : int { kSlotUnused = 0, kSlotPartial = 1, kSlotComplete = 2 };
+
 struct DecodeArgs {
     void* out;
     const void* q;
@@ -37,21 +62,22 @@ struct DecodeArgs {
     const void* v_cache;
     const int32_t* block_table;
     const int32_t* context_lens;
-    float* ws_acc;       // [B][H][max_parts][D]  (unused when max_parts == 1)
-    float* ws_m;         // [B][H][max_parts]
-    float* ws_l;         // [B][H][max_parts]
+    float* ws;           // workspace (header + partial slots)
     int32_t max_blocks;  // block_table row length
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
     int32_t num_blocks;
-    int32_t part_blocks; // partition size in blocks
-    int32_t max_parts;   // ceil(max_blocks / part_blocks): workspace slots per (seq, head)
-    int32_t splits;      // workgroups per (seq, kv-head group), 1 <= splits <= max_parts
+    int32_t group;       // num_heads / num_kv_heads
+    int32_t rh;          // query heads per run
+    int32_t runs;        // runs per sequence = num_heads / rh
+    int32_t part_blocks; // > 0: no work range covers more blocks than this (ranges are added)
+    int32_t nwv_cap;     // work ranges the workspace holds
+    int32_t slot_floats; // floats per partial slot
     float score_scale;   // scale * k_scale * log2(e): scores are kept in base-2 units
     float v_scale;       // 1 for f32 / bf16 pools
 };
 
-hipError_t launch_decode(int cache_dtype, int head_dim, int group, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -55,14 +55,10 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     return a.astype(np.float64)
 
 
-def pool_shape(w: W.Workload, layout: W.Layout):
-    return (layout.num_blocks, w.num_kv_heads, W.BLOCK_SIZE, w.head_dim)
-
-
 def oracle_pools(w: W.Workload, layout: W.Layout, with_new=True):
-    shp = pool_shape(w, layout)
-    kp = np.full(shp, POISON[w.cache_dtype], dtype=NP[w.cache_dtype])
-    vp = kp.copy()
+    nb, h, d, dt = layout.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype
+    kp = np.full(oracle.k_pool_shape(nb, h, d, dt), POISON[dt], dtype=NP[dt])
+    vp = np.full(oracle.v_pool_shape(nb, h, d, dt), POISON[dt], dtype=NP[dt])
     for b in layout.history:
         oracle.kv_write(b.k, b.v, w.in_dtype, kp, vp, w.cache_dtype, b.slots, k_scale=w.k_scale, v_scale=w.v_scale)
     if with_new:
@@ -72,10 +68,10 @@ def oracle_pools(w: W.Workload, layout: W.Layout, with_new=True):
 
 
 def gpu_pools(w: W.Workload, layout: W.Layout, with_new=True, poison=True):
-    shp = pool_shape(w, layout)
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
-    kp = torch.empty(shp, dtype=tdt, device="cuda")
-    vp = torch.empty(shp, dtype=tdt, device="cuda")
+    nb, h, d, dt = layout.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dt]
+    kp = torch.empty(pkv.k_cache_shape(nb, h, d, dt), dtype=tdt, device="cuda")
+    vp = torch.empty(pkv.v_cache_shape(nb, h, d, dt), dtype=tdt, device="cuda")
     if poison:
         if w.cache_dtype == "fp8":
             kp.fill_(0x7F); vp.fill_(0x7F)

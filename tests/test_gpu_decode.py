@@ -81,10 +81,11 @@ def test_zero_lengths_and_padding_rows(gpu):
 def test_empty_batch_is_noop(gpu):
     q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)
-    kc = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(pkv.k_cache_shape(4, 2, 128, "bf16"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(pkv.v_cache_shape(4, 2, 128), dtype=torch.bfloat16, device="cuda")
     bt = torch.empty((0, 3), dtype=torch.int32, device="cuda")
     cl = torch.empty((0,), dtype=torch.int32, device="cuda")
-    pkv.paged_attention_decode(out, q, kc, kc, bt, cl, 0.1)
+    pkv.paged_attention_decode(out, q, kc, vc, bt, cl, 0.1)
     torch.cuda.synchronize()
 
 
@@ -113,9 +114,9 @@ def test_single_token_fp8_every_code_bit_exact(gpu):
     vcodes = np.zeros((B, hkv, d), np.uint8)
     vcodes.reshape(-1)[:len(codes)] = codes
     NB = B
-    kc = torch.zeros((NB, hkv, 16, d), dtype=torch.uint8, device="cuda")
-    vc = torch.full((NB, hkv, 16, d), 0x7F, dtype=torch.uint8, device="cuda")
-    vc[:, :, 0, :] = torch.from_numpy(vcodes).cuda()
+    kc = torch.zeros(pkv.k_cache_shape(NB, hkv, d, "fp8"), dtype=torch.uint8, device="cuda")
+    vc = torch.full(pkv.v_cache_shape(NB, hkv, d), 0x7F, dtype=torch.uint8, device="cuda")
+    vc[:, :, :, 0] = torch.from_numpy(vcodes).cuda()  # token 0 of every dimension row
     bt = torch.arange(B, dtype=torch.int32, device="cuda").reshape(B, 1)
     cl = torch.ones(B, dtype=torch.int32, device="cuda")
     q = torch.randn((B, hq, d), device="cuda").to(torch.bfloat16)
@@ -141,10 +142,10 @@ def test_fp8_key_decode_scores(gpu):
     vals = oracle.fp8_decode(codes)
     # q has one non-zero dim; its magnitude makes |score| ~ 1 for every code
     scale = 1.0
-    kcodes = np.zeros((B, hkv, 16, d), np.uint8)
-    kcodes[:, 0, 1, 5] = codes                       # token 1, dim 5
-    vcodes = np.zeros((B, hkv, 16, d), np.uint8)
-    vcodes[:, 0, 1, 0] = 0x38                        # v1 = e_0 (value 1.0)
+    kcodes = np.zeros(oracle.k_pool_shape(B, hkv, d, "fp8"), np.uint8)   # [B, H, D/16, 16, 16]
+    kcodes[:, 0, 0, 1, 5] = codes                    # token 1, dim 5 (chunk 0)
+    vcodes = np.zeros(oracle.v_pool_shape(B, hkv, d, "fp8"), np.uint8)   # [B, H, D, 16]
+    vcodes[:, 0, 0, 1] = 0x38                        # v1 = e_0 (value 1.0)
     qv = np.zeros((B, hq, d), np.float32)
     qmag = (1.0 / np.abs(vals)).astype(np.float32)
     for h in range(hq):

@@ -53,17 +53,20 @@ def test_fp8_quantiser_bit_exact_sweep(gpu, scale):
     NB = (T + 15) // 16
     slots = np.arange(T, dtype=np.int32)
     _gpu.note(f"fp8 quantiser sweep scale={scale} n={x.size}")
-    kc = torch.full((NB, H, 16, D), 0x55, dtype=torch.uint8, device="cuda")
-    vc = torch.full((NB, H, 16, D), 0x55, dtype=torch.uint8, device="cuda")
+    kc = torch.full(pkv.k_cache_shape(NB, H, D, "fp8"), 0x55, dtype=torch.uint8, device="cuda")
+    vc = torch.full(pkv.v_cache_shape(NB, H, D), 0x55, dtype=torch.uint8, device="cuda")
     kd = _gpu.to_dev(k_new, "f32")
     pkv.paged_kv_write(kd, kd, kc, vc, _gpu.to_dev(slots, "i32"), scale, scale)
     torch.cuda.synchronize()
-    got = _gpu.to_host(kc, "fp8").reshape(NB * 16, D)[:T].reshape(-1)
     s32 = float(np.float32(scale))
     want = oracle.fp8_quantise(x, s32)
     nan = np.isnan(x)
-    assert np.array_equal(got[~nan], want[~nan])
-    assert np.all((got[nan] & 0x7F) == 0x7F)
+    # token rows back from the chunked K tile [NB, 1, D/16, 16, 16] and the dimension-major V tile [NB, 1, D, 16]
+    gk = _gpu.to_host(kc, "fp8").transpose(0, 1, 3, 2, 4).reshape(NB * 16, D)[:T].reshape(-1)
+    gv = _gpu.to_host(vc, "fp8").transpose(0, 1, 3, 2).reshape(NB * 16, D)[:T].reshape(-1)
+    for got in (gk, gv):
+        assert np.array_equal(got[~nan], want[~nan])
+        assert np.all((got[nan] & 0x7F) == 0x7F)
 
 
 def test_write_skips_negative_and_out_of_range_slots(gpu):
@@ -72,22 +75,26 @@ def test_write_skips_negative_and_out_of_range_slots(gpu):
     k = rng.standard_normal((6, H, D)).astype(np.float32)
     slots = np.array([-1, 3, NB * 16, 17, -5, 63], dtype=np.int32)  # two skipped, one past the pool
     _gpu.note("write skip/out-of-range slots")
-    kc = torch.full((NB, H, 16, D), 7.0, device="cuda")
-    vc = torch.full((NB, H, 16, D), 7.0, device="cuda")
+    kc = torch.full(pkv.k_cache_shape(NB, H, D, "f32"), 7.0, device="cuda")
+    vc = torch.full(pkv.v_cache_shape(NB, H, D), 7.0, device="cuda")
     kd = _gpu.to_dev(k, "f32")
     pkv.paged_kv_write(kd, kd, kc, vc, _gpu.to_dev(slots, "i32"))
     torch.cuda.synchronize()
-    got = kc.cpu().numpy()
+    # logical [NB, H, 16, D] views of the chunked K tile and the dimension-major V tile
+    got_k = kc.cpu().numpy().transpose(0, 1, 3, 2, 4).reshape(NB, H, 16, D)
+    got_v = vc.cpu().numpy().transpose(0, 1, 3, 2)
     want = np.full((NB, H, 16, D), 7.0, np.float32)
     for i, sl in enumerate(slots):
         if 0 <= sl < NB * 16:
             want[sl // 16, :, sl % 16, :] = k[i]
-    assert np.array_equal(got, want)
+    assert np.array_equal(got_k, want)
+    assert np.array_equal(got_v, want)
 
 
 def test_write_empty_is_noop(gpu):
-    kc = torch.zeros((2, 1, 16, 64), device="cuda")
+    kc = torch.zeros(pkv.k_cache_shape(2, 1, 64, "f32"), device="cuda")
+    vc = torch.zeros(pkv.v_cache_shape(2, 1, 64), device="cuda")
     e = torch.empty((0, 1, 64), device="cuda")
-    pkv.paged_kv_write(e, e, kc, kc.clone(), torch.empty((0,), dtype=torch.int32, device="cuda"))
+    pkv.paged_kv_write(e, e, kc, vc, torch.empty((0,), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.count_nonzero(kc).item() == 0
