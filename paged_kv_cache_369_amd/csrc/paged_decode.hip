@@ -494,7 +494,12 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a) {
 // Workgroup v - 1 handles the boundary at the first unit of range v when that
 // unit is inside a run and no earlier boundary cuts the same run; the
 // contributions are the previous range's last segment, then the first
-// segments of ranges v, v+1, ... while they continue the run.
+// segments of ranges v, v+1, ... while they continue the run.  The headers of
+// the next few ranges and then all contributions' states are requested
+// together, so a merge costs two memory round trips (plus one per further
+// batch of ranges for runs spread over many ranges).
+constexpr int kFixBatch = 4;  // ranges examined per round trip
+
 template <int QT, int D>
 __global__ __launch_bounds__(64) void paged_fixup_kernel(DecodeArgs a) {
     constexpr int EPL = D / 64;  // dimensions per lane
@@ -502,12 +507,21 @@ __global__ __launch_bounds__(64) void paged_fixup_kernel(DecodeArgs a) {
     const int nwv = reinterpret_cast<const int*>(a.ws)[1];
     const int v = blockIdx.x + 1;
     if (v >= nwv) return;
-    const int* sh = slot_ptr(a, v, 0);
-    const int* ph = slot_ptr(a, v - 1, 0);
-    const int s = sh[0], hg = sh[1];
-    if (sh[4] != kSlotPartial || sh[2] == 0) return;
-    const bool prev_same = ph[4] == kSlotPartial && ph[0] == s && ph[1] == hg;
-    if (prev_same && ph[2] > 0) return;
+    // headers: previous range (both slots) and ranges v .. v+kFixBatch-1 (slot 0)
+    const int4 p0 = *reinterpret_cast<const int4*>(slot_ptr(a, v - 1, 0));
+    const int pk0 = slot_ptr(a, v - 1, 0)[4];
+    int4 hb[kFixBatch];
+    int kb[kFixBatch];
+#pragma unroll
+    for (int i = 0; i < kFixBatch; ++i) {
+        const int x = min(v + i, nwv - 1);
+        hb[i] = *reinterpret_cast<const int4*>(slot_ptr(a, x, 0));
+        kb[i] = slot_ptr(a, x, 0)[4];
+    }
+    const int s = hb[0].x, hg = hb[0].y;
+    if (kb[0] != kSlotPartial || hb[0].z == 0) return;  // range v starts a run (or holds none cut)
+    const bool prev_same = pk0 == kSlotPartial && p0.x == s && p0.y == hg;
+    if (prev_same && p0.z > 0) return;  // an earlier boundary cuts this run
 
     float M[kMaxRunHeads], den[kMaxRunHeads], num[kMaxRunHeads][EPL];
 #pragma unroll
@@ -517,28 +531,48 @@ __global__ __launch_bounds__(64) void paged_fixup_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) num[h][e] = 0.0f;
     }
-    for (int x = v - 1; x < nwv; ++x) {
-        const int* xh = slot_ptr(a, x, (x == v - 1 && !prev_same) ? 1 : 0);
-        if (x > v && !(xh[4] == kSlotPartial && xh[0] == s && xh[1] == hg)) break;
-        const float* f = reinterpret_cast<const float*>(xh);
+    auto merge = [&](const float* f) {
+        float mx[kMaxRunHeads], lx[kMaxRunHeads], ax[kMaxRunHeads][EPL];
 #pragma unroll
         for (int h = 0; h < kMaxRunHeads; ++h) {
             if (h < a.rh) {
-                const float mx = f[8 + h];
-                const float lx = f[8 + kMaxRunHeads + h];
-                float ax[EPL];
+                mx[h] = f[8 + h];
+                lx[h] = f[8 + kMaxRunHeads + h];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) ax[e] = f[kSlotHead + h * D + lane + 64 * e];
-                if (mx != kNegInf) {
-                    const float Mn = fmaxf(M[h], mx);
-                    const float so = __builtin_amdgcn_exp2f(M[h] - Mn);  // 0 while M is -inf
-                    const float sn = __builtin_amdgcn_exp2f(mx - Mn);
-                    den[h] = den[h] * so + lx * sn;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) num[h][e] = num[h][e] * so + ax[e] * sn;
-                    M[h] = Mn;
-                }
+                for (int e = 0; e < EPL; ++e) ax[h][e] = f[kSlotHead + h * D + lane + 64 * e];
             }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxRunHeads; ++h) {
+            if (h < a.rh && mx[h] != kNegInf) {
+                const float Mn = fmaxf(M[h], mx[h]);
+                const float so = __builtin_amdgcn_exp2f(M[h] - Mn);  // 0 while M is -inf
+                const float sn = __builtin_amdgcn_exp2f(mx[h] - Mn);
+                den[h] = den[h] * so + lx[h] * sn;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) num[h][e] = num[h][e] * so + ax[h][e] * sn;
+                M[h] = Mn;
+            }
+        }
+    };
+    merge(reinterpret_cast<const float*>(slot_ptr(a, v - 1, prev_same ? 0 : 1)));
+    // ranges v, v+1, ... whose first segment continues the run
+    int x = v;
+    while (true) {
+        int n = 0;  // continuing ranges in this batch
+#pragma unroll
+        for (int i = 0; i < kFixBatch; ++i)
+            if (n == i && x + i < nwv && kb[i] == kSlotPartial && hb[i].x == s && hb[i].y == hg) n = i + 1;
+#pragma unroll
+        for (int i = 0; i < kFixBatch; ++i)
+            if (i < n) merge(reinterpret_cast<const float*>(slot_ptr(a, x + i, 0)));
+        if (n < kFixBatch) break;
+        x += kFixBatch;
+#pragma unroll
+        for (int i = 0; i < kFixBatch; ++i) {
+            const int y = min(x + i, nwv - 1);
+            hb[i] = *reinterpret_cast<const int4*>(slot_ptr(a, y, 0));
+            kb[i] = slot_ptr(a, y, 0)[4];
         }
     }
 #pragma unroll
