@@ -183,7 +183,7 @@ def summarize_traffic(args) -> int:
     fetch = _per_kernel(args.dec_fetch, "FETCH_SIZE")
     write = _per_kernel(args.dec_write, "WRITE_SIZE")
     kernels = {}
-    for key in ("paged_decode_kernel", "paged_fixup_kernel"):
+    for key in ("paged_decode_kernel",):
         f_kib, w_kib = _pick(fetch, key), _pick(write, key)
         kernels[key] = {"fetch_kib": f_kib, "write_kib": w_kib,
                         "fetch_bytes": f_kib * 1024 * fscale, "write_bytes": w_kib * 1024 * wscale}
@@ -318,7 +318,7 @@ def main() -> int:
     cl = _dev(w.context_lens, "i32", torch)
     ws_bytes = pkv.paged_attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                                    w.max_blocks_per_seq, W.BLOCK_SIZE, part)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
     def write():
@@ -382,7 +382,7 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "decode call: paged_decode_kernel + paged_fixup_kernel",
+                     "kernel": "paged_decode_kernel (the whole decode call)",
                      "avg_us": dec_us,
                      "algorithmic_bytes_per_call": kv_bytes},
         "write_us": float(np.mean(t_write)),

@@ -72,7 +72,8 @@ typedef enum pkv_status {
 
 /* Version of this ABI (incremented on any incompatible change; 2 = the
  * chunked-K / dimension-major-V pool layout and the workspace query that
- * takes num_kv_heads). */
+ * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
+ * use and is left that way by every call). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -111,10 +112,10 @@ int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
 /*
  * paged_attention_workspace_bytes -- bytes of device workspace that
  * paged_attention_decode needs for these sizes (host; no device call).  The
- * workspace holds a small header and the partial softmax states of the runs
+ * workspace holds arrival counters and the partial softmax states of the runs
  * (sequence, group of query heads sharing a KV head) that the balanced work
- * split cuts between waves: two states per work range, 4096 ranges, or more
- * when partition_size caps the blocks a range covers.
+ * split cuts between waves: two states per persistent wave (at most 4096
+ * waves), so the size depends on the head grouping and head_dim only.
  * partition_size as in paged_attention_decode.  Returns 0 for arguments
  * paged_attention_decode would reject.
  */
@@ -145,16 +146,21 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * k_scale,
  * v_scale        fp8 pool scales (ignored for F32/BF16 pools).
  * partition_size split-K granularity: 0 = balanced split only (the context
- *                blocks of all runs are cut into as many equal work ranges
- *                as the chip runs waves), otherwise a positive multiple of
- *                16: no work range covers more than partition_size tokens
- *                (more ranges are made).  A run cut between ranges has its
- *                partial states merged by a second kernel.  The split
- *                changes rounding only.
+ *                blocks of all runs are cut into as many equal stretches as
+ *                the chip runs waves), otherwise a positive multiple of 16:
+ *                each stretch is further cut into equal partitions of at most
+ *                partition_size tokens.  Every partition of a run gets its own
+ *                softmax state (m, l, acc) and a run's states are merged with
+ *                the rule M = max m_i, out = sum 2^(m_i-M) acc_i / sum
+ *                2^(m_i-M) l_i (in registers within a wave, through the
+ *                workspace between waves, by the last wave to finish its
+ *                part; no second launch).  The split changes rounding only;
+ *                for fixed sizes and lengths the result is deterministic.
  * workspace      device buffer of >= paged_attention_workspace_bytes(...)
- *                bytes, owned by the caller, contents need no
- *                initialisation; calls that share a workspace must be
- *                ordered (same stream).
+ *                bytes, owned by the caller, 16-byte aligned, zero-filled
+ *                before its first use (every call that completes leaves its
+ *                counters at zero again, so it is reused without clearing);
+ *                calls that share a workspace must be ordered (same stream).
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (also when
  * num_seqs * runs * max_blocks_per_seq >= 2^31), PKV_ERR_ALIGNMENT,
  * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  num_seqs == 0 is a no-op.

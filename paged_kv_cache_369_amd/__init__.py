@@ -148,10 +148,31 @@ def paged_attention_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads:
                                                        max_blocks_per_seq, block_size, partition_size))
 
 
+_WORKSPACES = {}
+
+
+def _default_workspace(device, need: int):
+    """A zero-filled workspace per device, grown on demand.  The decode leaves
+    its counters at zero, so the buffer is reused without clearing; calls on
+    different streams of one device that use it must not overlap (pass a
+    workspace of your own for that)."""
+    import torch
+    key = (device.type, device.index)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float,
                            k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
                            workspace=None, stream=None) -> None:
-    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the paged context of sequence s."""
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the paged context of sequence s.
+
+    workspace: uint8 device tensor of at least paged_attention_workspace_bytes(...)
+    bytes, zero-filled before its first use (torch.zeros); None uses a shared
+    per-device buffer."""
     import torch
     lib = _load()
     B, Hq, D = q.shape
@@ -163,7 +184,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
     MB = block_table.shape[1]
     need = paged_attention_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _default_workspace(q.device, need)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.paged_attention_decode(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),

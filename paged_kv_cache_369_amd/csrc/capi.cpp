@@ -9,26 +9,11 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool known_dtype(int dt) { return dt == PKV_DTYPE_F32 || dt == PKV_DTYPE_BF16 || dt == PKV_DTYPE_FP8_E4M3; }
-
-// Work ranges the decode may create for these sizes (the workspace holds two
-// partial-state slots per range): one per persistent wave, or more when a
-// partition size caps the blocks one range covers.  -1: invalid arguments.
-int64_t max_ranges(int32_t num_seqs, int32_t runs, int32_t max_blocks_per_seq, int32_t partition_size) {
-    if (partition_size < 0 || (partition_size % pkv::kBlockTokens) != 0) return -1;
-    int64_t n = pkv::kMaxWaves;
-    if (partition_size > 0) {
-        const int64_t pb = partition_size / pkv::kBlockTokens;
-        const int64_t units = int64_t(num_seqs) * runs * max_blocks_per_seq;
-        const int64_t need = (units + pb - 1) / pb;
-        n = need > n ? need : n;
-    }
-    return n;
-}
 
 }  // namespace
 
@@ -92,10 +77,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
         max_blocks_per_seq < 0 || block_size != pkv::kBlockTokens)
         return 0;
-    const int rh = pkv::run_heads(num_heads / num_kv_heads);
-    const int64_t nr = max_ranges(num_seqs, num_heads / rh, max_blocks_per_seq, partition_size);
-    if (nr < 0) return 0;
-    return size_t(pkv::kWsHeader + 2 * nr * pkv::slot_floats(rh, head_dim)) * sizeof(float);
+    if (partition_size < 0 || partition_size % pkv::kBlockTokens != 0) return 0;
+    return size_t(pkv::workspace_floats(pkv::run_heads(num_heads / num_kv_heads), head_dim)) * sizeof(float);
 }
 
 int paged_attention_decode(void* out,
@@ -139,9 +122,6 @@ int paged_attention_decode(void* out,
     const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
                                                         max_blocks_per_seq, block_size, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    const int64_t slot = pkv::slot_floats(rh, head_dim);
-    int64_t cap = (int64_t(workspace_bytes / sizeof(float)) - pkv::kWsHeader) / (2 * slot);
-    cap = cap < 0x7fffffff ? cap : 0x7fffffff;
 
     pkv::DecodeArgs a;
     a.out = out;
@@ -160,8 +140,7 @@ int paged_attention_decode(void* out,
     a.rh = rh;
     a.runs = runs;
     a.part_blocks = partition_size / pkv::kBlockTokens;
-    a.nwv_cap = int32_t(cap);
-    a.slot_floats = int32_t(slot);
+    a.slot_floats = int32_t(pkv::slot_floats(rh, head_dim));
     const float log2e = 1.4426950408889634f;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? v_scale : 1.0f;

@@ -16,13 +16,21 @@
 // sequence together with the rh query heads that share one KV head; it needs
 // every block of that sequence's KV head once.  Units are (sequence, run,
 // logical block) in that order; U is their total.  The launch is a persistent
-// grid of one-wave workgroups sized to the chip, and the unit line is cut
-// into nwv ranges of equal length (floor(v U / nwv) .. floor((v+1) U / nwv)),
-// range v going to wave v mod grid.  So every wave streams the same number of
-// KV tiles whatever the length mix, there is no tail of long sequences, and
-// short sequences cost no empty workgroups.  A range covers whole runs in its
-// middle (written out directly) and at most two partial runs at its ends,
-// whose states go to the workspace; paged_fixup_kernel merges them.
+// grid of one-wave workgroups sized to the chip, and wave w takes the
+// contiguous stretch [floor(w U / nw), floor((w+1) U / nw)) of the unit line.
+// So every wave streams the same number of KV tiles whatever the length mix,
+// there is no tail of long sequences, and short sequences cost no empty
+// workgroups.  With a partition size, the stretch is further cut into equal
+// partitions of at most that many blocks; each partition of a run gets its
+// own softmax state and the states are merged in order.
+//
+// Split-K reduction without a second launch.  A run that crosses a stretch
+// boundary gets one partial state from each wave it touches.  Those waves
+// combine their states in a tree of fan-in kMergeFanIn: a wave stores its
+// state in the workspace and counts itself in its group's arrival counter;
+// the wave that completes a group merges the group's states (in index order,
+// so the result does not depend on arrival order) and carries the merged
+// state to the next level, and the last one writes the output.
 //
 // Per block a wave
 //   1. loads the K tile (16-byte loads; the chunked K layout makes each load
@@ -117,8 +125,13 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s) {
     return a.num_blocks <= 0 ? 0 : L;  // no pool: every block is out of range
 }
 
-__device__ __forceinline__ int* slot_ptr(const DecodeArgs& a, int v, int k) {
-    return reinterpret_cast<int*>(a.ws + kWsHeader + (int64_t(v) * 2 + k) * a.slot_floats);
+// Partial-state slot k (0, 1) of wave w, and arrival counter idx of merge level lvl.
+__device__ __forceinline__ float* slot_ptr(const DecodeArgs& a, uint32_t w, int k) {
+    return a.ws + kWsHeader + kMergeLevels * kMaxWaves + (int64_t(w) * 2 + k) * a.slot_floats;
+}
+
+__device__ __forceinline__ int* counter_ptr(const DecodeArgs& a, int lvl, uint32_t idx) {
+    return reinterpret_cast<int*>(a.ws) + kWsHeader + lvl * kMaxWaves + idx;
 }
 
 template <int QT, int D>
@@ -130,6 +143,124 @@ __device__ void zero_rows(const DecodeArgs& a, int s) {
     } else {
         uint2* o = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + int64_t(s) * n);
         for (int i = lane_id(); i < n / 4; i += 64) o[i] = make_uint2(0u, 0u);
+    }
+}
+
+// Softmax state of a run over some of its tokens, in the matrix-core output
+// layout: lane (col, g) holds head col's running maximum m (base 2) and
+// normaliser l, both replicated over g, and acc[c] = dimensions 16c + 4g ..
+// 16c + 4g + 3 of the unnormalised output.  Lanes with col >= rh carry no head.
+template <int NVC>
+struct State {
+    float m, l;
+    f32x4 acc[NVC];
+};
+
+template <int NVC>
+__device__ __forceinline__ void state_clear(State<NVC>& s) {
+    s.m = kNegInf;
+    s.l = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) s.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// s <- merge(s, t): M = max(m_s, m_t), each side weighted by 2^(m - M)
+// (weight 0 for a side without scores).  Merging into a cleared state copies
+// t exactly.
+template <int NVC>
+__device__ __forceinline__ void state_merge(State<NVC>& s, const State<NVC>& t) {
+    const float M = fmaxf(s.m, t.m);
+    const float ws = s.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s.m - M);
+    const float wt = t.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(t.m - M);
+    s.m = M;
+    s.l = s.l * ws + t.l * wt;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) s.acc[c] = s.acc[c] * ws + t.acc[c] * wt;
+}
+
+// Slot traffic between waves uses agent-coherent accesses (SC1: stores write
+// through and loads miss in the caches that are not coherent across the
+// device), so a state is published by waiting for its stores before the
+// arrival is counted, with no cache-wide write-back or invalidation.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kAgentCoherent = 16;  // SC1 cache-policy bit
+constexpr unsigned kRawBufferWord3 = 0x00020000u;
+
+template <int D, int NVC>
+__device__ __forceinline__ void state_store(float* f, int slot_bytes, const State<NVC>& s, bool hv) {
+    const int lane = lane_id(), g = lane >> 4, col = lane & 15;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(f, 0, slot_bytes, kRawBufferWord3);
+    if (!hv) return;
+    if (g == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.m), r, col * 4, 0, kAgentCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.l), r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent);
+    }
+    const int ab = (kSlotHead + col * D + 4 * g) * 4;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r, ab + 64 * c, 0, kAgentCoherent);
+}
+
+template <int D, int NVC>
+__device__ __forceinline__ void state_load(const float* f, int slot_bytes, State<NVC>& s, bool hv) {
+    const int lane = lane_id(), g = lane >> 4;
+    const int col = hv ? (lane & 15) : 0;  // lanes without a head read head 0's data and never store it
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(f), 0, slot_bytes, kRawBufferWord3);
+    s.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, col * 4, 0, kAgentCoherent));
+    s.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent));
+    const int ab = (kSlotHead + col * D + 4 * g) * 4;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+        s.acc[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * c, 0, kAgentCoherent));
+}
+
+// A wave's merged state of the partitions it has finished of the current run
+// waits in LDS (lane-major, conflict-free) while the next partition streams,
+// so it occupies no registers in the streaming loop.
+template <int NVC>
+struct LdsState {
+    float m[64], l[64], acc[4 * NVC][64];
+};
+
+template <int NVC>
+__device__ __forceinline__ void lds_put(LdsState<NVC>& x, const State<NVC>& s) {
+    const int lane = lane_id();
+    x.m[lane] = s.m;
+    x.l[lane] = s.l;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x.acc[4 * c + r][lane] = s.acc[c][r];
+}
+
+template <int NVC>
+__device__ __forceinline__ void lds_get(const LdsState<NVC>& x, State<NVC>& s) {
+    const int lane = lane_id();
+    s.m = x.m[lane];
+    s.l = x.l[lane];
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.acc[c][r] = x.acc[4 * c + r][lane];
+}
+
+// out[s][head0 + col][:] = v_scale * acc / l (0 for a run without scores).
+template <int QT, int D, int NVC>
+__device__ __forceinline__ void state_output(const DecodeArgs& a, int s, int head0, const State<NVC>& st, bool hv) {
+    const int lane = lane_id(), g = lane >> 4, col = lane & 15;
+    if (!hv) return;
+    const float inv = st.l > 0.0f ? a.v_scale / st.l : 0.0f;
+    const int64_t o = (int64_t(s) * a.num_heads + head0 + col) * D + 4 * g;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) {
+        const f32x4 r = st.acc[c] * inv;
+        if constexpr (QT == kF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + 16 * c) = make_float4(r[0], r[1], r[2], r[3]);
+        } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o + 16 * c) =
+                make_uint2(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]));
+        }
     }
 }
 
@@ -172,12 +303,9 @@ __device__ __forceinline__ int cursor_next(Cursor& c, const DecodeArgs& a, int i
     return __builtin_ctzll(m);
 }
 
-// One segment: blocks [j0, j1) of run (s, hg).  slot < 0: the segment is the
-// whole run and the wave writes the output; otherwise the partial state goes
-// to workspace slot `slot` (range v, end k) with its header.
+// One segment: the softmax state of run (s, hg) over its blocks [j0, j1).
 template <int KV, int D, int P>
-__device__ void run_segment(const DecodeArgs& a, int s, int L, int hg, int j0, int j1, int slot_v, int slot_k,
-                            bool complete) {
+__device__ void run_segment(const DecodeArgs& a, int s, int L, int hg, int j0, int j1, State<Geo<KV, D>::NVC>& st) {
     using GE = Geo<KV, D>;
     using T = Tile<KV, D>;
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
@@ -357,237 +485,249 @@ __device__ void run_segment(const DecodeArgs& a, int s, int L, int hg, int j0, i
         }
     }
 
-    // ---- segment result ----
+    // ---- segment state: normaliser summed over the four row groups ----
     float lt = lsum + __shfl_xor(lsum, 16);
     lt += __shfl_xor(lt, 32);
-    if (complete) {
-        if (hv) {
-            const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-            const int64_t o = (int64_t(s) * a.num_heads + head0 + col) * D + 4 * g;
+    st.m = m;
+    st.l = lt;
 #pragma unroll
-            for (int c = 0; c < GE::NVC; ++c) {
-                const f32x4 r = acc[c] * inv;
-                if constexpr (QT == kF32) {
-                    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + 16 * c) = make_float4(r[0], r[1], r[2], r[3]);
-                } else {
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o + 16 * c) =
-                        make_uint2(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]));
-                }
-            }
-        }
-        if (slot_k == 0 && lane == 0) {  // the range's first segment was a whole run
-            int* h = slot_ptr(a, slot_v, 0);
-            h[0] = s; h[1] = hg; h[2] = j0; h[3] = j1; h[4] = kSlotComplete;
-        }
-    } else {
-        int* h = slot_ptr(a, slot_v, slot_k);
-        float* f = reinterpret_cast<float*>(h);
-        if (lane == 0) {
-            h[0] = s; h[1] = hg; h[2] = j0; h[3] = j1; h[4] = kSlotPartial;
-        }
-        if (hv) {
-            if (g == 0) {
-                f[8 + col] = m;
-                f[8 + kMaxRunHeads + col] = lt;
-            }
-            float* ab = f + kSlotHead + col * D + 4 * g;
-#pragma unroll
-            for (int c = 0; c < GE::NVC; ++c)
-                *reinterpret_cast<float4*>(ab + 16 * c) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-        }
-    }
+    for (int c = 0; c < GE::NVC; ++c) st.acc[c] = acc[c];
 }
 
-// Range geometry, identical in every wave: the unit line [0, U) is cut into
-// n equal ranges (range v = [floor(v U / n), floor((v+1) U / n))), one per
-// persistent wave or, under a partition cap, as many as keep every range
-// within part_blocks units; every range holds at least one unit.
-struct Ranges {
-    uint32_t U, n;
-    __device__ uint32_t count() const { return n; }
-    __device__ void bounds(uint32_t v, uint32_t& lo, uint32_t& hi) const {
-        lo = uint32_t(uint64_t(v) * U / n);
-        hi = uint32_t(uint64_t(v + 1) * U / n);
-    }
+// Stretch geometry, identical in every wave: nw waves, wave w owns units
+// [lo(w), lo(w + 1)), lo(w) = floor(w U / nw); every stretch holds at least
+// one unit (nw <= U).
+struct Split {
+    uint32_t U, nw;
+    __device__ uint32_t lo(uint32_t w) const { return uint32_t(uint64_t(w) * U / nw); }
+    // the wave whose stretch holds unit u: the largest w with lo(w) <= u
+    __device__ uint32_t wave_of(uint32_t u) const { return uint32_t((uint64_t(u + 1) * nw - 1) / U); }
 };
 
-__device__ __forceinline__ Ranges make_ranges(const DecodeArgs& a, uint32_t U, uint32_t nwt) {
-    Ranges r;
-    r.U = U;
-    uint32_t n = nwt;
-    if (a.part_blocks > 0) {
-        const uint32_t need = (U + uint32_t(a.part_blocks) - 1) / uint32_t(a.part_blocks);
-        n = need > n ? need : n;
-    }
-    n = n < uint32_t(a.nwv_cap) ? n : uint32_t(a.nwv_cap);
-    r.n = n < U ? n : U;
-    return r;
+// Combine the partial states of a run cut between waves and write its output.
+// The run's units [run_first, run_last] touch waves w0..w1; the wave with index
+// i = w - w0 among them holds state st.  Contributor i keeps its state in slot
+// 0 of wave w0 + i, except contributor 0 when the run starts after w0's first
+// unit (then the run is w0's last, not its first, run: slot 1).  A level-l node
+// n of the tree lives in the slot of contributor n * kMergeFanIn^l: the node
+// that completes group n at level l - 1 has merged that slot's previous
+// contents before it stores there.
+struct Contrib {
+    uint32_t w0, w1;
+    bool first_in_slot1;
+};
+
+__device__ __forceinline__ Contrib contributors(const Split& sp, uint32_t run_first, uint32_t run_last) {
+    return Contrib{sp.wave_of(run_first), sp.wave_of(run_last), run_first != sp.lo(sp.wave_of(run_first))};
 }
 
-// Process one work range: its segments in unit order.
+// Arrivals already counted in this wave's first merge group, read while the
+// wave still streams its last segment of the run (lane 0; -1: no group).
+__device__ __forceinline__ int peek_arrivals(const DecodeArgs& a, const Contrib& c, uint32_t w) {
+    const uint32_t idx = w - c.w0;
+    const uint32_t first = idx / kMergeFanIn * kMergeFanIn;
+    const uint32_t cnt = c.w1 - c.w0 + 1;
+    if (min(cnt, first + kMergeFanIn) - first <= 1) return -1;
+    int seen = -1;
+    if (lane_id() == 0)
+        seen = __hip_atomic_load(counter_ptr(a, 0, c.w0 + first), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return seen;
+}
+
+template <int QT, int D, int NVC>
+__device__ void merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, int s, int head0,
+                             const State<NVC>& mine, LdsState<NVC>& own_state, bool hv, int seen) {
+    auto slot = [&](uint32_t i) { return slot_ptr(a, c.w0 + i, (i == 0 && c.first_in_slot1) ? 1 : 0); };
+    const int slot_bytes = a.slot_floats * 4;
+    seen = __builtin_amdgcn_readfirstlane(seen);
+    lds_put(own_state, mine);  // this wave's node state waits in LDS between the steps below
+    uint32_t idx = w - c.w0, cnt = c.w1 - c.w0 + 1, span = 1;
+    for (int lvl = 0; cnt > 1; ++lvl) {
+        const uint32_t first = idx / kMergeFanIn * kMergeFanIn;
+        const uint32_t members = min(cnt, first + kMergeFanIn) - first;
+        if (members > 1) {
+            int* ctr = counter_ptr(a, lvl, c.w0 + first * span);
+            // Every other member had counted itself before this wave's last
+            // segment began: it is the last arrival and need not publish.
+            bool last = lvl == 0 && uint32_t(seen) == members - 1;
+            if (!last) {
+                {
+                    State<NVC> t;
+                    lds_get(own_state, t);
+                    state_store<D>(slot(idx * span), slot_bytes, t, hv);
+                }
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_s_waitcnt(0);  // the state has reached the coherent level before it is counted
+                int old = 0;
+                if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = __builtin_amdgcn_readfirstlane(old);
+                last = uint32_t(old) == members - 1;
+            }
+            if (!last) return;  // a later arrival completes the group
+            if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below are issued after the count was seen
+            // members in index order, two states per round trip; this wave's own from LDS
+            const uint32_t own = idx - first;
+            State<NVC> res;
+            state_clear(res);
+#pragma unroll 1
+            for (uint32_t r = 0; r < members; r += 2) {
+                State<NVC> in[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint32_t k = min(r + t, members - 1);
+                    state_load<D>(slot((first + k) * span), slot_bytes, in[t], hv);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint32_t k = r + t;
+                    if (k < members) {
+                        if (k == own) {
+                            State<NVC> o;
+                            lds_get(own_state, o);
+                            state_merge(res, o);
+                        } else {
+                            state_merge(res, in[t]);
+                        }
+                    }
+                }
+            }
+            lds_put(own_state, res);
+        }
+        idx /= kMergeFanIn;
+        cnt = (cnt + kMergeFanIn - 1) / kMergeFanIn;
+        span *= kMergeFanIn;
+    }
+    State<NVC> out;
+    lds_get(own_state, out);
+    state_output<QT, D>(a, s, head0, out, hv);
+}
+
+constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round trip
+
 template <int KV, int D, int P>
-__device__ void run_range(const DecodeArgs& a, Cursor& cur, const Ranges& rg, uint32_t v) {
-    uint32_t lo, hi;
-    rg.bounds(v, lo, hi);
+__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a) {
+    using GE = Geo<KV, D>;
+    constexpr int QT = (KV == kF32) ? kF32 : kBF16;
+    constexpr int NVC = GE::NVC;
+    const uint32_t w = blockIdx.x;
+    const uint32_t nwt = gridDim.x;
+    const int lane = lane_id();
+    const bool hv = (lane & 15) < a.rh;
+
+    // ---- total units; per-chunk totals of the first kLenChunks chunks; rows
+    //      of empty sequences are zeroed (sequence s by wave s mod grid) ----
+    uint32_t U = 0;
+    uint32_t ctot[kLenChunks];
+#pragma unroll
+    for (int c = 0; c < kLenChunks; ++c) ctot[c] = 0;
+    for (int base = 0; base < a.num_seqs; base += 64 * kLenChunks) {
+        int len[kLenChunks];
+#pragma unroll
+        for (int c = 0; c < kLenChunks; ++c) {
+            const int s = base + 64 * c + lane;
+            len[c] = s < a.num_seqs ? clamped_len(a, s) : 0;
+        }
+#pragma unroll
+        for (int c = 0; c < kLenChunks; ++c) {
+            const int cb = base + 64 * c;
+            if (cb >= a.num_seqs) break;
+            const uint32_t units = uint32_t((len[c] + kBlockTokens - 1) / kBlockTokens) * uint32_t(a.runs);
+            const uint32_t t = __builtin_amdgcn_readlane(wave_scan(units), 63);
+            if (base == 0) ctot[c] = t;
+            U += t;
+            unsigned long long empty = __ballot(cb + lane < a.num_seqs && len[c] == 0);
+            while (empty) {
+                const int se = cb + __builtin_ctzll(empty);
+                empty &= empty - 1;
+                if (uint32_t(se) % nwt == w) zero_rows<QT, D>(a, se);
+            }
+        }
+    }
+    const Split sp{U, U < nwt ? U : nwt};
+    if (w >= sp.nw) return;
+    const uint32_t lo = sp.lo(w), hi = sp.lo(w + 1);
+
+    // ---- the sequence holding unit lo: skip whole cached chunks, then walk ----
+    Cursor cur;
+    cur.start = 0;
+    int chunk = 0;
+    {
+        bool go = true;
+#pragma unroll
+        for (int c = 0; c < kLenChunks; ++c) {
+            go = go && cur.start + ctot[c] <= lo;
+            if (go) {
+                cur.start += ctot[c];
+                chunk = c + 1;
+            }
+        }
+    }
+    cursor_load(cur, a, 64 * chunk);
     int i = cursor_find(cur, a, lo);
     int L = __builtin_amdgcn_readlane(cur.len, i);
     int nb = (L + kBlockTokens - 1) / kBlockTokens;
-    const uint32_t first_unit = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - uint32_t(nb * a.runs);
-    const uint32_t rem = lo - first_unit;
-    int hg = int(rem / uint32_t(nb));
-    int j = int(rem % uint32_t(nb));
+    const uint32_t seq_first = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - uint32_t(nb * a.runs);
+    int hg = int((lo - seq_first) / uint32_t(nb));
+    int j = int((lo - seq_first) % uint32_t(nb));
+    uint32_t run_first = seq_first + uint32_t(hg * nb);
+
+    // ---- partitions: kk equal pieces of the stretch, each <= part_blocks ----
+    const uint32_t len = hi - lo;
+    const uint32_t kk = a.part_blocks > 0 ? (len + uint32_t(a.part_blocks) - 1) / uint32_t(a.part_blocks) : 1u;
+    uint32_t piece = 1;
+    uint32_t cut = lo + uint32_t(uint64_t(len) / kk);
+
+    __shared__ LdsState<NVC> held;  // merged state of the current run's finished partitions
+    bool holding = false;
     uint32_t u = lo;
-    int k = 0;
     while (true) {
-        const int j1 = int(min(uint32_t(nb), uint32_t(j) + (hi - u)));
-        const bool complete = (j == 0 && j1 == nb);
-        run_segment<KV, D, P>(a, cur.base + i, L, hg, j, j1, int(v), k, complete);
-        u += uint32_t(j1 - j);
-        if (u >= hi) break;
-        k = 1;
+        const int s = cur.base + i;
+        const uint32_t run_end = run_first + uint32_t(nb);
+        const uint32_t seg_end = run_end < cut ? run_end : cut;
+        const int j1 = j + int(seg_end - u);
+        // this segment ends the wave's part of the run: the run is finished
+        // here if it lies in the stretch, else it is merged with other waves
+        const bool ends_part = seg_end == run_end || seg_end == hi;
+        const bool local = run_first >= lo && seg_end == run_end;
+        Contrib cb{0, 0, false};
+        int seen = -1;
+        if (ends_part && !local) {
+            cb = contributors(sp, run_first, run_end - 1);
+            seen = peek_arrivals(a, cb, w);
+        }
+        State<NVC> st;
+        run_segment<KV, D, P>(a, s, L, hg, j, j1, st);
+        if (holding) {  // earlier partitions first
+            State<NVC> prev;
+            lds_get(held, prev);
+            state_merge(prev, st);
+            st = prev;
+        }
+        u = seg_end;
+        if (u == cut && u < hi) {
+            ++piece;
+            cut = lo + uint32_t(uint64_t(piece) * len / kk);
+        }
+        if (!ends_part) {
+            lds_put(held, st);  // a partition boundary inside the run
+            holding = true;
+            j = j1;
+            continue;
+        }
+        holding = false;
+        if (local)
+            state_output<QT, D>(a, s, hg * a.rh, st, hv);
+        else
+            merge_across<QT, D>(a, cb, w, s, hg * a.rh, st, held, hv, seen);
+        if (u == hi) break;
         j = 0;
+        run_first = run_end;
         if (++hg == a.runs) {
             hg = 0;
             i = cursor_next(cur, a, i);
             L = __builtin_amdgcn_readlane(cur.len, i);
             nb = (L + kBlockTokens - 1) / kBlockTokens;
-        }
-    }
-}
-
-template <int KV, int D, int P>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a) {
-    constexpr int QT = (KV == kF32) ? kF32 : kBF16;
-    const int w = blockIdx.x;
-    const int nwt = gridDim.x;
-
-    // total units; rows of empty sequences are zeroed (sequence s by wave s mod grid)
-    Cursor cur;
-    cur.start = 0;
-    uint32_t U = 0;
-    for (int base = 0; base < a.num_seqs; base += 64) {
-        cursor_load(cur, a, base);
-        U += cur.tot;
-        unsigned long long empty = __ballot(base + lane_id() < a.num_seqs && cur.len == 0);
-        while (empty) {
-            const int se = base + __builtin_ctzll(empty);
-            empty &= empty - 1;
-            if (se % nwt == w) zero_rows<QT, D>(a, se);
-        }
-    }
-    const Ranges rg = make_ranges(a, U, uint32_t(nwt));
-    if (w == 0 && lane_id() == 0) {
-        int* h = reinterpret_cast<int*>(a.ws);
-        h[0] = int(U);
-        h[1] = int(rg.count());
-    }
-    if (U == 0) return;
-
-    cur.start = 0;
-    cursor_load(cur, a, 0);
-    for (uint32_t v = uint32_t(w); v < rg.count(); v += uint32_t(nwt)) run_range<KV, D, P>(a, cur, rg, v);
-}
-
-// Merge the partial states of each run cut by a range boundary:
-// M = max_i m_i, out = v_scale * sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i
-// (taken online over the contributions, all heads of the run at once).
-// Workgroup v - 1 handles the boundary at the first unit of range v when that
-// unit is inside a run and no earlier boundary cuts the same run; the
-// contributions are the previous range's last segment, then the first
-// segments of ranges v, v+1, ... while they continue the run.  The headers of
-// the next few ranges and then all contributions' states are requested
-// together, so a merge costs two memory round trips (plus one per further
-// batch of ranges for runs spread over many ranges).
-constexpr int kFixBatch = 4;  // ranges examined per round trip
-
-template <int QT, int D>
-__global__ __launch_bounds__(64) void paged_fixup_kernel(DecodeArgs a) {
-    constexpr int EPL = D / 64;  // dimensions per lane
-    const int lane = lane_id();
-    const int nwv = reinterpret_cast<const int*>(a.ws)[1];
-    const int v = blockIdx.x + 1;
-    if (v >= nwv) return;
-    // headers: previous range (both slots) and ranges v .. v+kFixBatch-1 (slot 0)
-    const int4 p0 = *reinterpret_cast<const int4*>(slot_ptr(a, v - 1, 0));
-    const int pk0 = slot_ptr(a, v - 1, 0)[4];
-    int4 hb[kFixBatch];
-    int kb[kFixBatch];
-#pragma unroll
-    for (int i = 0; i < kFixBatch; ++i) {
-        const int x = min(v + i, nwv - 1);
-        hb[i] = *reinterpret_cast<const int4*>(slot_ptr(a, x, 0));
-        kb[i] = slot_ptr(a, x, 0)[4];
-    }
-    const int s = hb[0].x, hg = hb[0].y;
-    if (kb[0] != kSlotPartial || hb[0].z == 0) return;  // range v starts a run (or holds none cut)
-    const bool prev_same = pk0 == kSlotPartial && p0.x == s && p0.y == hg;
-    if (prev_same && p0.z > 0) return;  // an earlier boundary cuts this run
-
-    float M[kMaxRunHeads], den[kMaxRunHeads], num[kMaxRunHeads][EPL];
-#pragma unroll
-    for (int h = 0; h < kMaxRunHeads; ++h) {
-        M[h] = kNegInf;
-        den[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) num[h][e] = 0.0f;
-    }
-    auto merge = [&](const float* f) {
-        float mx[kMaxRunHeads], lx[kMaxRunHeads], ax[kMaxRunHeads][EPL];
-#pragma unroll
-        for (int h = 0; h < kMaxRunHeads; ++h) {
-            if (h < a.rh) {
-                mx[h] = f[8 + h];
-                lx[h] = f[8 + kMaxRunHeads + h];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) ax[h][e] = f[kSlotHead + h * D + lane + 64 * e];
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < kMaxRunHeads; ++h) {
-            if (h < a.rh && mx[h] != kNegInf) {
-                const float Mn = fmaxf(M[h], mx[h]);
-                const float so = __builtin_amdgcn_exp2f(M[h] - Mn);  // 0 while M is -inf
-                const float sn = __builtin_amdgcn_exp2f(mx[h] - Mn);
-                den[h] = den[h] * so + lx[h] * sn;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) num[h][e] = num[h][e] * so + ax[h][e] * sn;
-                M[h] = Mn;
-            }
-        }
-    };
-    merge(reinterpret_cast<const float*>(slot_ptr(a, v - 1, prev_same ? 0 : 1)));
-    // ranges v, v+1, ... whose first segment continues the run
-    int x = v;
-    while (true) {
-        int n = 0;  // continuing ranges in this batch
-#pragma unroll
-        for (int i = 0; i < kFixBatch; ++i)
-            if (n == i && x + i < nwv && kb[i] == kSlotPartial && hb[i].x == s && hb[i].y == hg) n = i + 1;
-#pragma unroll
-        for (int i = 0; i < kFixBatch; ++i)
-            if (i < n) merge(reinterpret_cast<const float*>(slot_ptr(a, x + i, 0)));
-        if (n < kFixBatch) break;
-        x += kFixBatch;
-#pragma unroll
-        for (int i = 0; i < kFixBatch; ++i) {
-            const int y = min(x + i, nwv - 1);
-            hb[i] = *reinterpret_cast<const int4*>(slot_ptr(a, y, 0));
-            kb[i] = slot_ptr(a, y, 0)[4];
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < kMaxRunHeads; ++h) {
-        if (h < a.rh) {
-            const int64_t o = (int64_t(s) * a.num_heads + hg * a.rh + h) * D + lane;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float r = den[h] > 0.0f ? (num[h][e] / den[h]) * a.v_scale : 0.0f;
-                if constexpr (QT == kF32) {
-                    static_cast<float*>(a.out)[o + 64 * e] = r;
-                } else {
-                    static_cast<uint16_t*>(a.out)[o + 64 * e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
-                }
-            }
         }
     }
 }
@@ -619,7 +759,6 @@ int device_cus() {
 
 template <int KV, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int QT = (KV == kF32) ? kF32 : kBF16;
     constexpr int P = Depth<KV, D>::P;
     auto kern = paged_decode_kernel<KV, D, P>;
     static int waves_per_cu = 0;  // occupancy of this instance (64-thread workgroups)
@@ -633,17 +772,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 #endif
     int nwt = waves_per_cu * device_cus();
     nwt = nwt < kMaxWaves ? nwt : kMaxWaves;
-    nwt = nwt < a.nwv_cap ? nwt : a.nwv_cap;
     hipLaunchKernelGGL(kern, dim3(nwt), dim3(64), 0, stream, a);
-    // one fix-up workgroup per range boundary the decode may create
-    int64_t ranges = nwt;
-    if (a.part_blocks > 0) {
-        const int64_t umax = int64_t(a.num_seqs) * a.runs * a.max_blocks;
-        ranges = std::max<int64_t>(ranges, (umax + a.part_blocks - 1) / a.part_blocks);
-    }
-    ranges = std::min<int64_t>(ranges, a.nwv_cap);
-    if (ranges > 1)
-        hipLaunchKernelGGL((paged_fixup_kernel<QT, D>), dim3(unsigned(ranges - 1)), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -46,14 +46,21 @@ inline int run_heads(int group) {
     return 1;
 }
 
-// Workspace: a 16-word header (word 0: total units, word 1: work ranges)
-// followed by two partial-state slots per work range.  Slot layout (floats):
-// 8 header words {seq, run, first block, end block, kind, -, -, -}, m[16],
-// l[16], acc[run_heads][D].
+// Workspace (caller-owned, zero-filled before its first use; every call that
+// completes leaves its counters at zero again):
+//   kWsHeader reserved words,
+//   kMergeLevels x kMaxWaves int32 arrival counters (one per merge group),
+//   two partial-state slots per wave: slot 0 for the run a wave continues from
+//   the wave before it, slot 1 for the run it hands on to the waves after it.
+// Slot layout (floats): m[16], l[16], acc[run_heads][D].
 constexpr int kWsHeader = 16;
-constexpr int kSlotHead = 8 + 2 * kMaxRunHeads;
+constexpr int kMergeFanIn = 8;   // states one merge step combines
+constexpr int kMergeLevels = 4;  // kMergeFanIn^kMergeLevels >= kMaxWaves
+constexpr int kSlotHead = 2 * kMaxRunHeads;
 inline int64_t slot_floats(int rh, int head_dim) { return kSlotHead + int64_t(rh) * head_dim; }
-enum SlotKind : int { kSlotUnused = 0, kSlotPartial = 1, kSlotComplete = 2 };
+inline int64_t workspace_floats(int rh, int head_dim) {
+    return kWsHeader + int64_t(kMergeLevels) * kMaxWaves + 2 * int64_t(kMaxWaves) * slot_floats(rh, head_dim);
+}
 
 struct DecodeArgs {
     void* out;
@@ -62,7 +69,7 @@ struct DecodeArgs {
     const void* v_cache;
     const int32_t* block_table;
     const int32_t* context_lens;
-    float* ws;           // workspace (header + partial slots)
+    float* ws;           // workspace (header, counters, partial-state slots)
     int32_t max_blocks;  // block_table row length
     int32_t num_seqs;
     int32_t num_heads;
@@ -71,8 +78,7 @@ struct DecodeArgs {
     int32_t group;       // num_heads / num_kv_heads
     int32_t rh;          // query heads per run
     int32_t runs;        // runs per sequence = num_heads / rh
-    int32_t part_blocks; // > 0: no work range covers more blocks than this (ranges are added)
-    int32_t nwv_cap;     // work ranges the workspace holds
+    int32_t part_blocks; // > 0: partitions of at most this many blocks, each with its own softmax state
     int32_t slot_floats; // floats per partial slot
     float score_scale;   // scale * k_scale * log2(e): scores are kept in base-2 units
     float v_scale;       // 1 for f32 / bf16 pools

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     for st in range(6):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -97,29 +97,29 @@ def test_decode_validation(lib):
     assert _dec(lib, q=A + 4) == ALIGN
     assert _dec(lib, cl=A + 2) == ALIGN
     need = lib.paged_attention_workspace_bytes(4, 32, 8, 128, 64, 16, 0)
-    assert need == _ws(R0, 4, 128)
+    assert need == _ws(4, 128)
     assert _dec(lib, ws=0, wsb=0) == WORKSPACE
     assert _dec(lib, wsb=need - 1) == WORKSPACE
     assert _dec(lib, B=0) == OK                        # empty batch: no launch
 
 
-def _ws(ranges, run_heads, d):
-    """Header (16 words) + two partial-state slots per work range of 8 + 32 + run_heads * D floats."""
-    return (16 + 2 * ranges * (8 + 32 + run_heads * d)) * 4
+def _ws(run_heads, d):
+    """Header (16 words) + 4 merge levels x 4096 arrival counters + two
+    partial-state slots per persistent wave (4096 at most) of 32 + run_heads * D floats."""
+    return (16 + 4 * W + 2 * W * (32 + run_heads * d)) * 4
 
 
 W = 4096                   # persistent waves (upper bound)
-R0 = W                     # ranges without a partition cap: one per wave
 
 
 def test_workspace_sizes(lib):
     ws = lib.paged_attention_workspace_bytes
-    assert ws(4, 8, 8, 128, 32, 16, 0) == _ws(R0, 1, 128)          # MHA: one head per run
-    assert ws(256, 32, 8, 128, 512, 16, 0) == _ws(R0, 4, 128)      # GQA group 4
-    assert ws(16, 64, 8, 128, 2048, 16, 512) == _ws(16 * 8 * 2048 // 32, 8, 128)  # 512-token cap: more ranges
-    assert ws(2, 8, 2, 64, 10, 16, 16) == _ws(R0, 4, 64)           # cap needs fewer ranges than the default
-    assert ws(2, 32, 1, 64, 10, 16, 0) == _ws(R0, 16, 64)          # group 32 -> runs of 16 heads
-    assert ws(2, 24, 1, 64, 10, 16, 0) == _ws(R0, 12, 64)          # group 24 -> runs of 12 heads
+    assert ws(4, 8, 8, 128, 32, 16, 0) == _ws(1, 128)          # MHA: one head per run
+    assert ws(256, 32, 8, 128, 512, 16, 0) == _ws(4, 128)      # GQA group 4
+    assert ws(16, 64, 8, 128, 2048, 16, 512) == _ws(8, 128)    # partitions do not need more space
+    assert ws(1 << 16, 64, 8, 128, 2048, 16, 0) == _ws(8, 128)  # nor does the batch
+    assert ws(2, 32, 1, 64, 10, 16, 0) == _ws(16, 64)          # group 32 -> runs of 16 heads
+    assert ws(2, 24, 1, 64, 10, 16, 0) == _ws(12, 64)          # group 24 -> runs of 12 heads
     assert ws(2, 8, 64, 64, 10, 16, 24) == 0           # invalid partition size
     assert ws(2, 8, 8, 64, 10, 8, 0) == 0              # invalid block size
     assert ws(2, 8, 3, 64, 10, 16, 0) == 0             # heads not a multiple of KV heads

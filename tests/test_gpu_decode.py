@@ -272,3 +272,37 @@ def test_out_of_range_table_entries_do_not_fault(gpu):
     _gpu.note("out-of-range table entries")
     pkv.paged_attention_decode(out, q, kp, vp, _gpu.to_dev(bt, "i32"), _gpu.to_dev(w.context_lens, "i32"), w.scale)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("hq,hkv,d,cache,part", [
+    (8, 8, 64, "f32", 0), (32, 8, 128, "bf16", 0), (32, 8, 128, "bf16", 512), (64, 8, 128, "fp8", 512),
+])
+def test_long_context_merge_tree(gpu, hq, hkv, d, cache, part):
+    """One long sequence beside short ones: its runs are cut over hundreds of
+    waves, so their partial states combine over several tree levels.  Parity
+    with the oracle, identical bits on a repeat call, and the workspace's
+    arrival counters are all zero again afterwards."""
+    in_dtype = "bf16" if cache == "fp8" else None
+    w = W.make_custom("chain", 71, [40000, 5, 3000, 1], hq, hkv, d, "f32" if cache == "f32" else "bf16", cache,
+                      partition_size=part, in_dtype=in_dtype)
+    _gpu.note(f"merge tree {cache} hq={hq} hkv={hkv} d={d} part={part}")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    need = pkv.paged_attention_workspace_bytes(w.num_seqs, hq, hkv, d, w.max_blocks_per_seq, 16, part)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    q = _gpu.to_dev(w.q, w.q_dtype)
+    bt = _gpu.to_dev(w.layout.block_table, "i32")
+    cl = _gpu.to_dev(w.context_lens, "i32")
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        pkv.paged_attention_decode(out, q, kp, vp, bt, cl, w.scale, w.k_scale, w.v_scale,
+                                   partition_size=part, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(_gpu.widen(_gpu.to_host(out, w.q_dtype), w.q_dtype))
+    assert np.array_equal(outs[0], outs[1])
+    counters = ws[64:64 + 4 * 4096 * 4].view(torch.int32)
+    assert int(torch.count_nonzero(counters)) == 0
+    ok, ov = _gpu.oracle_pools(w, w.layout)
+    want = _gpu.oracle_decode(w, w.layout, ok, ov)
+    err, where = _gpu.max_err(outs[0], want)
+    assert err <= _gpu.TOL[cache], (err, where)
