@@ -172,6 +172,49 @@ def _pick(per_kernel, key):
     return sum(vals) / len(vals) if vals else 0.0
 
 
+def summarize_counters(args) -> int:
+    """Markdown table of SQ/GRBM counters of the decode kernel (one or more --pmc runs)."""
+    vals = {}
+    for d in args.counter_dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if "paged_decode_kernel" not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no paged_decode_kernel rows in the counter runs")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    from paged_kv_cache_369_amd import workloads as W
+    lines = [f"# SQ counters of `paged_decode_kernel`, workload `{args.workload}`", "",
+             WORKLOAD_DESC[args.workload], "", "Commands (run from the repository root):", ""]
+    lines += [f"    {c}" for c in args.commands]
+    lines += ["", "Mean over the profiled dispatches (each counter summed over the device by rocprofv3).", "",
+              "| counter | value per dispatch |", "|---|---|"]
+    for k in sorted(mean):
+        lines.append(f"| `{k}` | {mean[k]:.6g} |")
+    derived = []
+    if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_LDS_IDX_ACTIVE", 0) > 0:
+        derived.append(f"- LDS bank-conflict cycles per LDS-active cycle (`SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE`): "
+                       f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.4f}")
+    if "SQ_INSTS_VMEM_RD" in mean and "SQ_WAVES" in mean and mean["SQ_WAVES"] > 0:
+        derived.append(f"- vector memory read instructions per wave (`SQ_INSTS_VMEM_RD / SQ_WAVES`): "
+                       f"{mean['SQ_INSTS_VMEM_RD'] / mean['SQ_WAVES']:.1f}")
+    if "SQ_INSTS_VALU" in mean and "SQ_WAVES" in mean and mean["SQ_WAVES"] > 0:
+        derived.append(f"- VALU instructions per wave (`SQ_INSTS_VALU / SQ_WAVES`): "
+                       f"{mean['SQ_INSTS_VALU'] / mean['SQ_WAVES']:.0f}")
+    if "SQ_WAVE_CYCLES" in mean and mean.get("SQ_BUSY_CYCLES", 0) > 0:
+        derived.append(f"- wave-cycles per busy SQ cycle (`SQ_WAVE_CYCLES / SQ_BUSY_CYCLES`): "
+                       f"{mean['SQ_WAVE_CYCLES'] / mean['SQ_BUSY_CYCLES']:.2f}")
+    if derived:
+        lines += ["", "Ratios:", ""] + derived
+    lines += ["", f"Decode source digest `{decode_source_digest()}`."]
+    os.makedirs(args.out_dir, exist_ok=True)
+    path = os.path.join(args.out_dir, f"paged_decode_{args.workload}_sq_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+    return 0
+
+
 def summarize_traffic(args) -> int:
     """Scale FETCH_SIZE / WRITE_SIZE of the decode call by the copy calibration; write profiles/ files."""
     cf = _pick(_per_kernel(args.copy_fetch, "FETCH_SIZE"), "copyBuffer")
@@ -265,6 +308,9 @@ def main() -> int:
                     help="instead of the decode step, run a plain device copy of known size (counter scale)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a markdown summary of a rocprofv3 --stats run")
     ap.add_argument("--summarize-traffic", action="store_true", help="write profiles/ HBM traffic summary")
+    ap.add_argument("--summarize-counters", action="store_true", help="write profiles/ SQ counter summary")
+    ap.add_argument("--counters", action="append", dest="counter_dirs", default=[],
+                    help="a rocprofv3 --pmc output directory (repeatable)")
     ap.add_argument("--out-dir", default=PROFILES, help="where --summarize-traffic writes")
     ap.add_argument("--copy-fetch"); ap.add_argument("--copy-write")
     ap.add_argument("--dec-fetch"); ap.add_argument("--dec-write")
@@ -274,6 +320,8 @@ def main() -> int:
 
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, " && ".join(args.commands))
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.summarize_traffic:
         return summarize_traffic(args)
 

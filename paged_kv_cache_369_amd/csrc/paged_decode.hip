@@ -605,8 +605,15 @@ __device__ void merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
 
 constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round trip
 
+// Waves per SIMD the register allocation must allow: two for the 16-bit and
+// 8-bit pools (the streaming loop fits in 256 registers), one for fp32 pools
+// of head_dim 128, whose tiles are twice as large.
+template <int KV, int D>
+constexpr int kWavesPerSimd = (KV == kF32 && D == 128) ? 1 : 2;
+
 template <int KV, int D, int P>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D>))) void paged_decode_kernel(
+    DecodeArgs a) {
     using GE = Geo<KV, D>;
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
     constexpr int NVC = GE::NVC;
