@@ -201,6 +201,9 @@ def summarize_counters(args) -> int:
     if "SQ_INSTS_VALU" in mean and "SQ_WAVES" in mean and mean["SQ_WAVES"] > 0:
         derived.append(f"- VALU instructions per wave (`SQ_INSTS_VALU / SQ_WAVES`): "
                        f"{mean['SQ_INSTS_VALU'] / mean['SQ_WAVES']:.0f}")
+    hits, misses = mean.get("TCC_HIT_sum", mean.get("TCC_HIT")), mean.get("TCC_MISS_sum", mean.get("TCC_MISS"))
+    if hits is not None and misses is not None and hits + misses > 0:
+        derived.append(f"- L2 hit rate (`TCC_HIT / (TCC_HIT + TCC_MISS)`): {hits / (hits + misses):.3f}")
     if "SQ_WAVE_CYCLES" in mean and mean.get("SQ_BUSY_CYCLES", 0) > 0:
         derived.append(f"- wave-cycles per busy SQ cycle (`SQ_WAVE_CYCLES / SQ_BUSY_CYCLES`): "
                        f"{mean['SQ_WAVE_CYCLES'] / mean['SQ_BUSY_CYCLES']:.2f}")
@@ -304,6 +307,9 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-oracle baseline and check (-1 = all, 0 = skip)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
+                    help="read (or overwrite) 512 MB before every step, outside the timed brackets, so the step's "
+                         "KV reads cannot hit what the previous step left in the 256 MB infinity cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode step, run a plain device copy of known size (counter scale)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a markdown summary of a rocprofv3 --stats run")
@@ -385,9 +391,19 @@ def main() -> int:
     # stream (torch's current stream, which the binding passes to the library)
     # bracket the write and the decode call of every step.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # --flush-mall: before every step, outside the event brackets, stream a buffer of twice the
+    # 256 MB infinity cache through it (reading, or writing), so the KV reads of the step cannot hit
+    # data the previous step left there
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if args.flush_mall else None
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda") if args.flush_mall else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in ev:
+        if flush is not None:
+            if args.flush_mall == "read":
+                torch.sum(flush, dim=0, out=flush_sink)
+            else:
+                flush.fill_(1.0)
         e[0].record()
         write()
         e[1].record()
@@ -396,6 +412,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    if flush is not None:  # the flush is not part of the step: time the step from its events
+        ms_per_step = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
     t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     dec_us = float(np.mean(t_dec))
@@ -425,7 +443,8 @@ def main() -> int:
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": W.BLOCK_SIZE, "kv_dtype": w.cache_dtype, "q_dtype": w.q_dtype,
                    "sum_context": int(w.context_lens.sum()),
-                   "partition_size": part, "kv_bytes": kv_bytes},
+                   "partition_size": part, "kv_bytes": kv_bytes, "kv_unique_bytes": w.kv_unique_bytes(),
+                   "mall_flush": args.flush_mall},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,

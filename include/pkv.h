@@ -177,6 +177,41 @@ int paged_attention_decode(void* out,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * pkv_check_inputs -- count the contents of the index arrays that the kernels
+ * treat as invalid.  The write and decode stay memory-safe for any contents
+ * (an out-of-range table entry is an empty block, a length is clamped into
+ * [0, max_blocks_per_seq*16], an out-of-range slot is skipped), so their
+ * results are simply unspecified for such inputs; this call says whether that
+ * happened.  A debug aid: one workgroup, and the repeat check is quadratic in
+ * num_tokens.
+ *   Source for what is valid: ipipp.com article §二 (the table maps each
+ *   logical block to a physical one); bytelighting wiki "vLLM", "Flattened
+ *   布局与 slot_mapping" (one slot per new token).
+ *
+ * block_table,
+ * context_lens   as in paged_attention_decode (may be NULL when num_seqs == 0;
+ *                block_table may be NULL when max_blocks_per_seq == 0).
+ * slot_mapping   as in paged_kv_write (may be NULL when num_tokens == 0).
+ * num_blocks     pool size in blocks.
+ * counts         device int32[4], 16-byte aligned, overwritten
+ *                asynchronously on `stream`:
+ *                  [0] sequences whose context_lens entry is < 0 or above
+ *                      max_blocks_per_seq*16;
+ *                  [1] table entries the decode reads (j < ceil(L/16), L
+ *                      clamped as above) outside [0, num_blocks);
+ *                  [2] slot_mapping entries that are neither -1 nor in
+ *                      [0, num_blocks*16);
+ *                  [3] slot_mapping entries >= 0 that repeat an earlier entry.
+ * Errors: PKV_ERR_INVALID_ARG (negative sizes, NULL counts or a NULL array
+ * with a non-zero size, size products >= 2^31), PKV_ERR_ALIGNMENT,
+ * PKV_ERR_HIP.
+ */
+int pkv_check_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs,
+                     const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_blocks, int32_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

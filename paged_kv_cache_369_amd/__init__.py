@@ -24,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes",
+__all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
            "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
 BLOCK_SIZE = 16
@@ -62,6 +62,8 @@ def _load():
     lib.paged_attention_decode.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p,
                                            i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
+    lib.pkv_check_inputs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -193,3 +195,23 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
                                     B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), float(k_scale), float(v_scale),
                                     int(partition_size), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "paged_attention_decode")
+
+
+def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_mapping=None, stream=None):
+    """Counts of invalid index-array contents (see include/pkv.h), read back after the launch:
+    (bad context lengths, bad table entries, bad slots, repeated slots)."""
+    import torch
+    dev = next((t.device for t in (block_table, context_lens, slot_mapping) if t is not None), None)
+    if dev is None:
+        raise ValueError("pass at least one of block_table/context_lens, slot_mapping")
+    counts = torch.empty(4, dtype=torch.int32, device=dev)
+    B = int(context_lens.shape[0]) if context_lens is not None else 0
+    MB = int(block_table.shape[1]) if block_table is not None else 0
+    T = int(slot_mapping.shape[0]) if slot_mapping is not None else 0
+    none = ctypes.c_void_p(0)
+    st = _load().pkv_check_inputs(_dev(block_table, "block_table") if block_table is not None else none, MB,
+                                  _dev(context_lens, "context_lens") if context_lens is not None else none, B,
+                                  _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else none, T,
+                                  int(num_blocks), _dev(counts, "counts"), _stream(stream))
+    _check(st, "pkv_check_inputs")
+    return tuple(int(x) for x in counts.cpu().tolist())

@@ -148,4 +148,29 @@ int paged_attention_decode(void* out,
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_check_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs,
+                     const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_blocks, int32_t* counts, void* stream) {
+    if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return PKV_ERR_INVALID_ARG;
+    if (!counts) return PKV_ERR_INVALID_ARG;
+    if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_table))) return PKV_ERR_INVALID_ARG;
+    if (num_tokens > 0 && !slot_mapping) return PKV_ERR_INVALID_ARG;
+    if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (!aligned(counts, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(slot_mapping, 4))
+        return PKV_ERR_ALIGNMENT;
+    pkv::CheckArgs a;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.slot_mapping = slot_mapping;
+    a.counts = counts;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_blocks = num_blocks;
+    const hipError_t e = pkv::launch_check(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // extern "C"

@@ -86,4 +86,17 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
+struct CheckArgs {
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    const int32_t* slot_mapping;
+    int32_t* counts;  // 4 int32, overwritten
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_tokens;
+    int32_t num_blocks;
+};
+
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+
 }  // namespace pkv

@@ -99,6 +99,16 @@ class Workload:
         """Bytes of K and V that attention must read: sum_s L_s * H_kv * D * 2 * elt."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * self.kv_elt_bytes()
 
+    def kv_unique_bytes(self) -> int:
+        """Bytes of the distinct cached tokens attention reads: a physical block shared by several sequences
+        (an aliased prefix) counts once, with the most tokens any of them uses."""
+        used = {}
+        for s, L in enumerate(self.context_lens.tolist()):
+            for j in range((L + 15) // 16):
+                b = int(self.layout.block_table[s, j])
+                used[b] = max(used.get(b, 0), min(16, L - 16 * j))
+        return sum(used.values()) * self.num_kv_heads * self.head_dim * 2 * self.kv_elt_bytes()
+
 
 # ---------------------------------------------------------------------------
 # value draws

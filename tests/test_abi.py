@@ -123,3 +123,23 @@ def test_workspace_sizes(lib):
     assert ws(2, 8, 64, 64, 10, 16, 24) == 0           # invalid partition size
     assert ws(2, 8, 8, 64, 10, 8, 0) == 0              # invalid block size
     assert ws(2, 8, 3, 64, 10, 16, 0) == 0             # heads not a multiple of KV heads
+
+
+def _chk(lib, **kw):
+    a = dict(bt=A, MB=8, cl=A, B=4, slot=A, T=4, NB=100, counts=A)
+    a.update(kw)
+    return lib.pkv_check_inputs(a["bt"], a["MB"], a["cl"], a["B"], a["slot"], a["T"], a["NB"], a["counts"], None)
+
+
+def test_check_inputs_validation(lib):
+    assert _chk(lib, B=-1) == INVALID
+    assert _chk(lib, T=-1) == INVALID
+    assert _chk(lib, MB=-1) == INVALID
+    assert _chk(lib, NB=-1) == INVALID
+    assert _chk(lib, counts=0) == INVALID
+    assert _chk(lib, cl=0) == INVALID                 # sequences without lengths
+    assert _chk(lib, bt=0) == INVALID                 # sequences with blocks but no table
+    assert _chk(lib, slot=0) == INVALID               # tokens without slots
+    assert _chk(lib, NB=1 << 27) == INVALID           # slots overflow int32
+    assert _chk(lib, counts=A + 4) == ALIGN
+    assert _chk(lib, cl=A + 2) == ALIGN
