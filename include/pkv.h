@@ -67,13 +67,15 @@ typedef enum pkv_status {
     PKV_ERR_UNSUPPORTED = 2,  /* a valid but unimplemented combination (dtype pair, head_dim, block_size) */
     PKV_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned */
     PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than paged_attention_workspace_bytes() */
-    PKV_ERR_HIP = 5           /* the HIP runtime reported an error while launching */
+    PKV_ERR_HIP = 5,          /* the HIP runtime reported an error while launching */
+    PKV_ERR_OUT_OF_BLOCKS = 6 /* the block manager has too few free blocks (nothing was changed) */
 } pkv_status;
 
 /* Version of this ABI (incremented on any incompatible change; 2 = the
  * chunked-K / dimension-major-V pool layout and the workspace query that
  * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
- * use and is left that way by every call). */
+ * use and is left that way by every call; 4 = the block manager and
+ * paged_kv_copy_blocks). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -211,6 +213,85 @@ int pkv_check_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t num_seqs,
                      const int32_t* slot_mapping, int32_t num_tokens,
                      int32_t num_blocks, int32_t* counts, void* stream);
+
+/*
+ * ---- Host block manager (no device calls) --------------------------------
+ *
+ * Hands out the 16-token blocks of a pool of num_blocks on demand, lets
+ * sequences share blocks (fork: parallel sampling, beam search), and gives a
+ * sequence a private copy of a shared, partly filled last block when it first
+ * writes into it (copy-on-write).  It produces the slot_mapping entries for
+ * paged_kv_write and the block_table rows and context_lens for
+ * paged_attention_decode.
+ *   Source: ai-maas.com vLLM article, 先看浪费在哪里 (blocks requested and
+ *   returned on demand instead of a max_len reservation per request);
+ *   ipipp.com article §二 (per-sequence block table; blocks shared between
+ *   sequences with reference counts; a shared block is copied when written).
+ *
+ * Allocation is deterministic: free blocks form a stack that starts as
+ * [num_blocks-1, ..., 1, 0], so block 0 is handed out first, and a block
+ * returns to the top when its last reference goes (a freed sequence releases
+ * its blocks in table order).  A copy-on-write queues a block copy (src ->
+ * dst); pending copies keep both blocks from being handed out until
+ * pkv_bm_take_copies returns them.  The caller must run the taken copies with
+ * paged_kv_copy_blocks on the stream before any later paged_kv_write.
+ * The manager is plain host state, owned by the caller, not thread-safe.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager for a pool of num_blocks blocks, at most max_blocks_per_seq per
+ * sequence.  NULL for negative sizes, num_blocks*16 >= 2^31, or no memory. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t max_blocks_per_seq);
+void pkv_bm_destroy(pkv_block_manager* m);
+
+/* A new empty sequence.  PKV_ERR_INVALID_ARG if seq_id exists. */
+int pkv_bm_add(pkv_block_manager* m, int64_t seq_id);
+
+/* child shares every block of parent (reference counts +1) and its length.
+ * PKV_ERR_INVALID_ARG if parent is unknown, child exists or they are equal. */
+int pkv_bm_fork(pkv_block_manager* m, int64_t parent, int64_t child);
+
+/* Reserve slots for n new tokens at the end of seq_id: slots_out[i] (host
+ * int32[n]) = block*16 + offset of token len+i.  Allocates blocks as needed
+ * and queues a copy when the last block is shared and partly filled.
+ * PKV_ERR_OUT_OF_BLOCKS (state unchanged) when the pool or max_blocks_per_seq
+ * is exhausted; PKV_ERR_INVALID_ARG for an unknown sequence or n < 0. */
+int pkv_bm_append(pkv_block_manager* m, int64_t seq_id, int32_t n, int32_t* slots_out);
+
+/* Drop seq_id; its blocks lose one reference each and are freed at zero. */
+int pkv_bm_free(pkv_block_manager* m, int64_t seq_id);
+
+/* Rows of the block table for n sequences: table_out (host int32
+ * [n][max_blocks]) gets each sequence's blocks, -1 padded; lens_out (host
+ * int32[n]) its length.  PKV_ERR_INVALID_ARG (nothing written) for an unknown
+ * sequence or one with more than max_blocks blocks. */
+int pkv_bm_table(const pkv_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                 int32_t* table_out, int32_t* lens_out);
+
+/* Take up to max_copies pending copies, oldest first, into src_out/dst_out
+ * (host int32[max_copies]); the batch stops before a copy that reads a block
+ * an earlier copy of the batch writes, so one paged_kv_copy_blocks call can
+ * run it in parallel (call again for the rest).  Returns the count, -1 on bad
+ * arguments. */
+int32_t pkv_bm_take_copies(pkv_block_manager* m, int32_t* src_out, int32_t* dst_out, int32_t max_copies);
+
+/* out (host int64[5]): free blocks, used blocks, live sequences, tokens held
+ * by the used blocks (a shared block counted once), pending copies. */
+int pkv_bm_stats(const pkv_block_manager* m, int64_t* out);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks of both pools, K and V of every
+ * KV head: block dst[i] <- block src[i] for i < n (the copies of a
+ * copy-on-write).  src, dst: device int32[n].  Pairs with an id outside
+ * [0, num_blocks) are skipped.  The destinations must be distinct and no
+ * destination may be another pair's source (pkv_bm_take_copies batches that
+ * way).  Asynchronous on `stream`; n == 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (dtype, head_dim,
+ * block_size), PKV_ERR_ALIGNMENT, PKV_ERR_HIP.
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, const int32_t* src, const int32_t* dst, int32_t n,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ import ctypes
 import os
 
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
+           "BlockManager", "paged_kv_copy_blocks",
            "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
 BLOCK_SIZE = 16
@@ -64,6 +65,26 @@ def _load():
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
     lib.pkv_check_inputs.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.pkv_bm_create.argtypes = [i32, i32]
+    lib.pkv_bm_create.restype = p
+    lib.pkv_bm_destroy.argtypes = [p]
+    lib.pkv_bm_destroy.restype = None
+    for name in ("pkv_bm_add", "pkv_bm_free"):
+        getattr(lib, name).argtypes = [p, i64]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pkv_bm_fork.argtypes = [p, i64, i64]
+    lib.pkv_bm_fork.restype = ctypes.c_int
+    lib.pkv_bm_append.argtypes = [p, i64, i32, p]
+    lib.pkv_bm_append.restype = ctypes.c_int
+    lib.pkv_bm_table.argtypes = [p, p, i32, i32, p, p]
+    lib.pkv_bm_table.restype = ctypes.c_int
+    lib.pkv_bm_take_copies.argtypes = [p, p, p, i32]
+    lib.pkv_bm_take_copies.restype = i32
+    lib.pkv_bm_stats.argtypes = [p, p]
+    lib.pkv_bm_stats.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [p, p, ctypes.c_int, i32, i32, i32, i32, p, p, i32, p]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -215,3 +236,75 @@ def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_
                                   int(num_blocks), _dev(counts, "counts"), _stream(stream))
     _check(st, "pkv_check_inputs")
     return tuple(int(x) for x in counts.cpu().tolist())
+
+
+class BlockManager:
+    """The library's host block manager (see include/pkv.h): blocks handed out on demand, sequences forked
+    with shared blocks, copy-on-write of a shared partly filled last block.  Host numpy arrays in and out."""
+
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int):
+        import numpy as np  # noqa: F401  (used by the methods)
+        self._lib = _load()
+        self._h = self._lib.pkv_bm_create(int(num_blocks), int(max_blocks_per_seq))
+        if not self._h:
+            raise PkvError(1, "pkv_bm_create")
+        self.num_blocks, self.max_blocks_per_seq = int(num_blocks), int(max_blocks_per_seq)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, seq: int):
+        _check(self._lib.pkv_bm_add(self._h, int(seq)), "pkv_bm_add")
+
+    def fork(self, parent: int, child: int):
+        _check(self._lib.pkv_bm_fork(self._h, int(parent), int(child)), "pkv_bm_fork")
+
+    def append(self, seq: int, n: int):
+        import numpy as np
+        slots = np.empty(max(int(n), 1), dtype=np.int32)
+        _check(self._lib.pkv_bm_append(self._h, int(seq), int(n), slots.ctypes.data), "pkv_bm_append")
+        return slots[: int(n)]
+
+    def free(self, seq: int):
+        _check(self._lib.pkv_bm_free(self._h, int(seq)), "pkv_bm_free")
+
+    def table(self, seqs, max_blocks: int):
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        tab = np.empty((max(len(ids), 1), max(int(max_blocks), 1)), dtype=np.int32)
+        lens = np.empty(max(len(ids), 1), dtype=np.int32)
+        _check(self._lib.pkv_bm_table(self._h, ids.ctypes.data, len(ids), int(max_blocks), tab.ctypes.data,
+                                      lens.ctypes.data), "pkv_bm_table")
+        return tab[: len(ids), : int(max_blocks)], lens[: len(ids)]
+
+    def take_copies(self, max_copies: int = 1 << 16):
+        import numpy as np
+        src = np.empty(max(int(max_copies), 1), dtype=np.int32)
+        dst = np.empty_like(src)
+        k = self._lib.pkv_bm_take_copies(self._h, src.ctypes.data, dst.ctypes.data, int(max_copies))
+        if k < 0:
+            raise PkvError(1, "pkv_bm_take_copies")
+        return src[:k].copy(), dst[:k].copy()
+
+    def stats(self):
+        import numpy as np
+        out = np.zeros(5, dtype=np.int64)
+        _check(self._lib.pkv_bm_stats(self._h, out.ctypes.data), "pkv_bm_stats")
+        return tuple(int(x) for x in out)
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
+    """Copy whole blocks of both pools: block dst[i] <- block src[i] (device int32 tensors)."""
+    NB, Hkv, D = _pools(k_cache, v_cache)
+    n = int(src.numel())
+    if dst.numel() != n:
+        raise ValueError("src and dst differ in length")
+    st = _load().paged_kv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache), Hkv,
+                                      D, BLOCK_SIZE, NB, _dev(src, "src") if n else ctypes.c_void_p(0),
+                                      _dev(dst, "dst") if n else ctypes.c_void_p(0), n, _stream(stream))
+    _check(st, "paged_kv_copy_blocks")

@@ -21,7 +21,7 @@ ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_SOURCES = ["kv_write.hip", "paged_decode.hip", "check.hip"]
-CXX_SOURCES = ["capi.cpp"]
+CXX_SOURCES = ["capi.cpp", "block_manager.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + CSRC, "-I" + os.path.join(HERE, "..", "include")]
 HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

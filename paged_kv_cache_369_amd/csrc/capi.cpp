@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -29,6 +29,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
     default: return "unknown status";
     }
 }
@@ -145,6 +146,28 @@ int paged_attention_decode(void* out,
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
     const hipError_t e = pkv::launch_decode(cache_dtype, head_dim, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, const int32_t* src, const int32_t* dst, int32_t n,
+                         void* stream) {
+    if (n < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0) return PKV_ERR_INVALID_ARG;
+    if (!known_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+    if (block_size != pkv::kBlockTokens || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+    if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (n == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !src || !dst) return PKV_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src, 4) || !aligned(dst, 4)) return PKV_ERR_ALIGNMENT;
+    pkv::CopyArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.src = src;
+    a.dst = dst;
+    a.n = n;
+    a.num_blocks = num_blocks;
+    a.block_bytes = int64_t(num_kv_heads) * pkv::kBlockTokens * head_dim * pkv::dtype_bytes(cache_dtype);
+    const hipError_t e = pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

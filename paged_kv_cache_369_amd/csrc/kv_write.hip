@@ -16,6 +16,8 @@
 // per dimension row).  The fp8 variant reads 16 input elements per thread and
 // quantises them with a bit-exact round-to-nearest-even, saturating E4M3
 // encoder.
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -171,6 +173,40 @@ hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const Wr
         else if (in_dtype == kBF16 && head_dim == 128) PKV_QUANT(kBF16, 128);
         else return hipErrorInvalidValue;
 #undef PKV_QUANT
+    }
+    return hipGetLastError();
+}
+
+namespace {
+
+// Block copies of a copy-on-write: one grid row per (src, dst) pair; a block
+// of one pool (all KV heads) is contiguous, so each pair is two plain copies
+// of block_bytes, done in 16-byte chunks.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, int pair0) {
+    const int pair = pair0 + int(blockIdx.y);
+    const int src = a.src[pair], dst = a.dst[pair];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+    const int64_t n16 = a.block_bytes / 16;
+    const uint4* ks = static_cast<const uint4*>(a.k_cache) + int64_t(src) * n16;
+    const uint4* vs = static_cast<const uint4*>(a.v_cache) + int64_t(src) * n16;
+    uint4* kd = static_cast<uint4*>(a.k_cache) + int64_t(dst) * n16;
+    uint4* vd = static_cast<uint4*>(a.v_cache) + int64_t(dst) * n16;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += int64_t(gridDim.x) * blockDim.x) {
+        const uint4 k = ks[i];
+        const uint4 v = vs[i];
+        kd[i] = k;
+        vd[i] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
+    const int64_t n16 = a.block_bytes / 16;
+    const unsigned gx = unsigned(std::min<int64_t>((n16 + 255) / 256, 16));
+    for (int pair0 = 0; pair0 < a.n; pair0 += 65535) {
+        const unsigned gy = unsigned(std::min(a.n - pair0, 65535));
+        hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream, a, pair0);
     }
     return hipGetLastError();
 }

@@ -37,6 +37,18 @@ struct WriteArgs {
 
 hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const WriteArgs& a, hipStream_t stream);
 
+struct CopyArgs {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t n;
+    int32_t num_blocks;
+    int64_t block_bytes;  // bytes of one block in one pool (all KV heads), a multiple of 16
+};
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
 // Query heads of one run: the largest divisor of the GQA group that is at
 // most kMaxRunHeads.  A run is (sequence, group of run_heads query heads that
 // share one KV head); each KV tile of the run is read once for all its heads.

@@ -278,11 +278,15 @@ def _lens_for(name: str, rng: np.random.Generator) -> np.ndarray:
     raise ValueError(name)
 
 
+def _prefix_private_lens(rng: np.random.Generator, n: int, priv_max: int) -> np.ndarray:
+    return rng.integers(1, priv_max, size=n, endpoint=True).astype(np.int32)
+
+
 def _make_prefix(seed: int, prompts: int = 32, samples: int = 8, prefix: int = 1024,
                  priv_max: int = 512, hq: int = 32, hkv: int = 8, d: int = 128) -> Workload:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(0,))))
     B = prompts * samples
-    priv = rng.integers(1, priv_max, size=B, endpoint=True).astype(np.int32)
+    priv = _prefix_private_lens(rng, B, priv_max)
     lens = (prefix + priv).astype(np.int32)
     pb = prefix // BLOCK_SIZE
     priv_blocks = [blocks_for(n) for n in priv]
@@ -345,6 +349,17 @@ def _make_prefix(seed: int, prompts: int = 32, samples: int = 8, prefix: int = 1
                     q_dtype="bf16", in_dtype="bf16", cache_dtype="bf16", context_lens=lens, q=q,
                     new_k=new_k, new_v=new_v, layout=shared, twin=twin,
                     scale=float(np.float32(1.0) / np.sqrt(np.float32(d))))
+
+
+def context_lengths(name: str, seed: Optional[int] = None) -> np.ndarray:
+    """The context lengths ``make(name, seed)`` gives, without drawing any values (fast at every size).
+    For "prefix" the samples of a prompt are consecutive, 8 to a prompt, each 1024 + its private length."""
+    seed = SEEDS[name] if seed is None else seed
+    if name == "prefix":
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(0,))))
+        return (1024 + _prefix_private_lens(rng, 32 * 8, 512)).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(9,))))
+    return _lens_for(name, rng)
 
 
 def make(name: str, seed: Optional[int] = None) -> Workload:

@@ -1,0 +1,126 @@
+"""The library's host block manager (C ABI, no GPU) against the reference model.
+
+Random operation sequences run on both; every returned slot list, taken copy
+batch, block-table row, length and statistic must be equal.  Host-side
+validation of the manager's entry points is checked too.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_369_amd as pkv
+from oracle.block_manager import OutOfBlocks, RefBlockManager
+
+OK, INVALID, OUT_OF_BLOCKS = 0, 1, 6
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_manager_matches_model(seed):
+    rnd = random.Random(1000 + seed)
+    nb, mbs = rnd.choice([(40, 10), (200, 30), (7, 7)])
+    lib, ref = pkv.BlockManager(nb, mbs), RefBlockManager(nb, mbs)
+    nxt = 0
+    for _ in range(300):
+        live = list(ref.seqs)
+        op = rnd.random()
+        if op < 0.15 or not live:
+            lib.add(nxt); ref.add(nxt); nxt += 1
+        elif op < 0.3:
+            p = rnd.choice(live)
+            lib.fork(p, nxt); ref.fork(p, nxt); nxt += 1
+        elif op < 0.7:
+            s, n = rnd.choice(live), rnd.choice([0, 1, 3, 16, 17, 50])
+            try:
+                want = ref.append(s, n)
+            except OutOfBlocks:
+                with pytest.raises(pkv.PkvError) as e:
+                    lib.append(s, n)
+                assert e.value.status == OUT_OF_BLOCKS
+                continue
+            assert lib.append(s, n).tolist() == want
+        elif op < 0.85:
+            s = rnd.choice(live)
+            lib.free(s); ref.release(s)
+        else:
+            k = rnd.choice([1, 2, 100])
+            src, dst = lib.take_copies(k)
+            assert list(zip(src.tolist(), dst.tolist())) == ref.take_copies(k)
+        assert lib.stats() == ref.stats()
+    live = sorted(ref.seqs)
+    if live:
+        tab, lens = lib.table(live, mbs)
+        rows, rlens = ref.table(live, mbs)
+        assert tab.tolist() == rows and lens.tolist() == rlens
+
+
+def test_manager_validation():
+    lib = pkv._load()
+    assert not lib.pkv_bm_create(-1, 4)
+    assert not lib.pkv_bm_create(1 << 27, 4)       # slots overflow int32
+    bm = pkv.BlockManager(4, 2)
+    h = bm._h
+    assert lib.pkv_bm_add(h, 5) == OK
+    assert lib.pkv_bm_add(h, 5) == INVALID          # exists
+    assert lib.pkv_bm_fork(h, 5, 5) == INVALID
+    assert lib.pkv_bm_fork(h, 9, 10) == INVALID     # unknown parent
+    assert lib.pkv_bm_append(h, 9, 1, None) == INVALID
+    assert lib.pkv_bm_append(h, 5, -1, None) == INVALID
+    assert lib.pkv_bm_append(h, 5, 1, None) == INVALID      # no slot buffer
+    assert lib.pkv_bm_append(h, 5, 0, None) == OK
+    slots = np.empty(40, dtype=np.int32)
+    assert lib.pkv_bm_append(h, 5, 33, slots.ctypes.data) == OUT_OF_BLOCKS   # 3 blocks > max 2 per sequence
+    assert lib.pkv_bm_free(h, 9) == INVALID
+    assert lib.pkv_bm_take_copies(h, None, None, -1) == -1
+    assert lib.pkv_status_string(OUT_OF_BLOCKS) == b"not enough free blocks"
+
+
+def test_copy_blocks_validation():
+    lib = pkv._load()
+    A = 0x100000
+    f = lambda **kw: lib.paged_kv_copy_blocks(kw.get("k", A), kw.get("v", A), kw.get("dt", 1), kw.get("H", 8),
+                                              kw.get("D", 128), kw.get("bs", 16), kw.get("NB", 10),
+                                              kw.get("src", A), kw.get("dst", A), kw.get("n", 3), None)
+    assert f(n=-1) == INVALID
+    assert f(dt=9) == INVALID
+    assert f(D=96) == 2
+    assert f(bs=8) == 2
+    assert f(src=0) == INVALID
+    assert f(k=A + 8) == 3
+    assert f(n=0) == OK
+
+
+def test_utilisation_report_matches_model():
+    """bench.py's utilisation report: the reserved / paged shares equal the reference model's, and the block
+    manager holding the shared-prefix workload (prompts forked into their samples) holds exactly the workload's
+    unique tokens, in as many blocks as the aliased layout uses."""
+    import importlib.util
+    import os
+
+    from oracle.block_manager import kv_utilisation
+    from paged_kv_cache_369_amd import workloads as W
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    rows = {r["workload"]: r for r in bench.utilisation_rows()}
+    for name, r in rows.items():
+        lens = W.context_lengths(name)
+        assert r["max_len"] >= int(lens.max())
+        res, paged = kv_utilisation(lens, r["max_len"])
+        assert r["reserved_util"] == pytest.approx(res, rel=1e-12)
+        assert r["paged_util"] == pytest.approx(paged, rel=1e-12)
+    assert rows["gqa8b"]["reserved_util"] < 0.3 and rows["gqa8b"]["paged_util"] > 0.99
+    # prefix: 32 prompts of 1024 shared tokens (64 blocks each), then each sample's private tokens
+    lens = W.context_lengths("prefix").astype(np.int64)
+    priv = lens - 1024
+    assert rows["prefix"]["shared_tokens_held"] == 32 * 1024 + int(priv.sum())
+    assert rows["prefix"]["shared_blocks_used"] == 32 * 64 + int(((priv + 15) // 16).sum())
+    assert rows["prefix"]["block_copies"] == 0          # the prefix ends on a block boundary
+
+
+def test_context_lengths_match_workloads():
+    from paged_kv_cache_369_amd import workloads as W
+    for name in ("tiny", "prefix"):
+        assert np.array_equal(W.context_lengths(name), W.make(name).context_lens), name
