@@ -75,7 +75,8 @@ typedef enum pkv_status {
  * chunked-K / dimension-major-V pool layout and the workspace query that
  * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
  * use and is left that way by every call; 4 = the block manager and
- * paged_kv_copy_blocks). */
+ * paged_kv_copy_blocks; 5 = paged_attention_decode_cascade and
+ * pkv_bm_shared_prefix). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -178,6 +179,71 @@ int paged_attention_decode(void* out,
                            int32_t partition_size,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * paged_attention_cascade_workspace_bytes -- workspace size for
+ * paged_attention_decode_cascade: the decode workspace with merge slots wide
+ * enough for a prefix run's columns, then two arrays of num_seqs * num_heads
+ * state rows of head_dim + 4 floats.  Grows with num_seqs.  The arrival
+ * counters of the prefix/suffix meeting live in the region every workspace
+ * reserves for counters, so one zero-filled buffer may serve plain and
+ * cascade calls of any shape in turn.  Returns 0 for arguments
+ * paged_attention_decode would reject.
+ */
+size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t partition_size);
+
+/*
+ * paged_attention_decode_cascade -- the same result as paged_attention_decode
+ * (up to rounding), reading each shared prefix block once for several of the
+ * sequences that share it instead of once per sequence.
+ *   Source: ai-maas.com article, 先看浪费在哪里 (parallel samples of one prompt
+ *   share one prefix); ipipp.com article §二 (sequences of a beam search or a
+ *   multi-turn chat have table entries pointing to the same physical blocks);
+ *   the result is attention over each sequence's own table, so sharing only
+ *   changes which reads serve which sequences.
+ *
+ * All arguments as in paged_attention_decode, plus:
+ * prefix_leader  [num_seqs] int32 device array: the first sequence of s's
+ *                sharing group.  A group is a run of consecutive sequences
+ *                with the same leader; prefix_leader[s] == s for a sequence
+ *                that shares nothing.
+ * prefix_blocks  [num_seqs] int32 device array: the number of leading logical
+ *                blocks s shares with every other member of its group (the
+ *                same physical block ids in the same table positions), equal
+ *                for all members; 0 = none.  Only whole blocks can be shared:
+ *                the kernel uses min(prefix_blocks[s], L_s / 16).
+ * The members of a group are served in chunks of 16 / (query heads per run)
+ * consecutive sequences (4 for a GQA group of 4, 16 for one query head per KV
+ * head): one prefix run per chunk and KV head reads the shared blocks through
+ * the chunk's first table row and scores them for all the chunk's heads at
+ * once.  Each sequence's remaining blocks are read by its own runs, and the
+ * two softmax states of every head are merged (same rule as partitions).
+ * A sequence whose entries disagree with its chunk's first sequence (another
+ * leader or shared length, a leader after it) is decoded on its own; results
+ * are unspecified (but memory-safe) when the shared blocks are in fact not the
+ * same.  Setting prefix_blocks to all zeros gives plain decode.
+ * workspace      >= paged_attention_cascade_workspace_bytes(...) bytes, with
+ *                the same zero-fill and reuse contract as for
+ *                paged_attention_decode.
+ * Errors: as paged_attention_decode (PKV_ERR_UNSUPPORTED also when the state
+ * rows need 2^31 bytes or more, or num_seqs * runs > 2^18, runs =
+ * num_heads / query heads per run); PKV_ERR_INVALID_ARG for NULL prefix
+ * arrays.
+ */
+int paged_attention_decode_cascade(void* out,
+                                   const void* q, int q_dtype,
+                                   const void* k_cache, const void* v_cache, int cache_dtype,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens,
+                                   const int32_t* prefix_leader, const int32_t* prefix_blocks,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   float scale, float k_scale, float v_scale,
+                                   int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * pkv_check_inputs -- count the contents of the index arrays that the kernels

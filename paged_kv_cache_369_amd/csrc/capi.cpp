@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -82,17 +82,22 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
     return size_t(pkv::workspace_floats(pkv::run_heads(num_heads / num_kv_heads), head_dim)) * sizeof(float);
 }
 
-int paged_attention_decode(void* out,
-                           const void* q, int q_dtype,
-                           const void* k_cache, const void* v_cache, int cache_dtype,
-                           const int32_t* block_table, int32_t max_blocks_per_seq,
-                           const int32_t* context_lens,
-                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                           float scale, float k_scale, float v_scale,
-                           int32_t partition_size,
-                           void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Sequences whose heads share one prefix run's matrix columns.
+int prefix_members(int rh) { return pkv::kMaxRunHeads / rh; }
+
+int64_t cascade_extra_floats(int64_t num_seqs, int num_heads, int head_dim) {
+    return 2 * pkv::align_floats(num_seqs * num_heads * pkv::state_row_floats(head_dim));
+}
+
+int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache, int cache_dtype,
+                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                float scale, float k_scale, float v_scale, int32_t partition_size, const int32_t* prefix_leader,
+                const int32_t* prefix_blocks, bool cascade, void* workspace, size_t workspace_bytes, void* stream) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         num_blocks < 0 || max_blocks_per_seq < 0)
         return PKV_ERR_INVALID_ARG;
@@ -110,21 +115,30 @@ int paged_attention_decode(void* out,
         return PKV_ERR_INVALID_ARG;
     if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
     if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    const int rh = pkv::run_heads(num_heads / num_kv_heads);
+    const int runs = num_heads / rh;
+    // units (sequence, run, block) are counted in 32 bits; a prefix run adds at most one sequence's worth
+    if (int64_t(num_seqs) * runs * max_blocks_per_seq * (cascade ? 2 : 1) >= (int64_t(1) << 31))
+        return PKV_ERR_UNSUPPORTED;
+    const int64_t state_bytes = int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim) * 4;
+    if (cascade && (state_bytes >= (int64_t(1) << 31) || int64_t(num_seqs) * runs > pkv::kMeetCounters))
+        return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
         return PKV_ERR_INVALID_ARG;
+    if (cascade && (!prefix_leader || !prefix_blocks)) return PKV_ERR_INVALID_ARG;
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(workspace, 16))
+        !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(workspace, 16) ||
+        !aligned(prefix_leader, 4) || !aligned(prefix_blocks, 4))
         return PKV_ERR_ALIGNMENT;
 
-    const int rh = pkv::run_heads(num_heads / num_kv_heads);
-    const int runs = num_heads / rh;
-    if (int64_t(num_seqs) * runs * max_blocks_per_seq >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
-    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                        max_blocks_per_seq, block_size, partition_size);
+    const size_t need = cascade ? paged_attention_cascade_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                                          max_blocks_per_seq, block_size, partition_size)
+                                : paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                                  max_blocks_per_seq, block_size, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
-    pkv::DecodeArgs a;
+    pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_cache = k_cache;
@@ -141,12 +155,75 @@ int paged_attention_decode(void* out,
     a.rh = rh;
     a.runs = runs;
     a.part_blocks = partition_size / pkv::kBlockTokens;
-    a.slot_floats = int32_t(pkv::slot_floats(rh, head_dim));
     const float log2e = 1.4426950408889634f;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? v_scale : 1.0f;
+    if (cascade) {
+        // a prefix run's columns hold `members` sequences' heads, so its slots are that wide
+        const int members = prefix_members(rh);
+        const int64_t base = pkv::workspace_floats(members * rh, head_dim);
+        a.slot_floats = int32_t(pkv::slot_floats(members * rh, head_dim));
+        a.prefix_leader = prefix_leader;
+        a.prefix_blocks = prefix_blocks;
+        a.members = members;
+        a.meet = reinterpret_cast<int32_t*>(a.ws + pkv::kWsHeader + int64_t(pkv::kMergeLevels) * pkv::kMaxWaves);
+        a.pstate = a.ws + base;
+        a.sstate = a.pstate + pkv::align_floats(int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim));
+        a.state_bytes = int32_t(state_bytes);
+    } else {
+        a.slot_floats = int32_t(pkv::slot_floats(rh, head_dim));
+    }
     const hipError_t e = pkv::launch_decode(cache_dtype, head_dim, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void* out,
+                           const void* q, int q_dtype,
+                           const void* k_cache, const void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
+                       partition_size, nullptr, nullptr, false, workspace, workspace_bytes, stream);
+}
+
+size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t partition_size) {
+    if (paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                                        partition_size) == 0)
+        return 0;
+    const int rh = pkv::run_heads(num_heads / num_kv_heads);
+    const int64_t f = pkv::workspace_floats(prefix_members(rh) * rh, head_dim) +
+                      cascade_extra_floats(num_seqs, num_heads, head_dim);
+    return size_t(f) * sizeof(float);
+}
+
+int paged_attention_decode_cascade(void* out,
+                                   const void* q, int q_dtype,
+                                   const void* k_cache, const void* v_cache, int cache_dtype,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens,
+                                   const int32_t* prefix_leader, const int32_t* prefix_blocks,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   float scale, float k_scale, float v_scale,
+                                   int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
+                       partition_size, prefix_leader, prefix_blocks, true, workspace, workspace_bytes, stream);
 }
 
 int paged_kv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_kv_heads, int32_t head_dim,

@@ -127,7 +127,7 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s) {
 
 // Partial-state slot k (0, 1) of wave w, and arrival counter idx of merge level lvl.
 __device__ __forceinline__ float* slot_ptr(const DecodeArgs& a, uint32_t w, int k) {
-    return a.ws + kWsHeader + kMergeLevels * kMaxWaves + (int64_t(w) * 2 + k) * a.slot_floats;
+    return a.ws + kSlotBase + (int64_t(w) * 2 + k) * a.slot_floats;
 }
 
 __device__ __forceinline__ int* counter_ptr(const DecodeArgs& a, int lvl, uint32_t idx) {
@@ -215,6 +215,39 @@ __device__ __forceinline__ void state_load(const float* f, int slot_bytes, State
         s.acc[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * c, 0, kAgentCoherent));
 }
 
+// State rows of the shared-prefix meeting: one row per (sequence, head) with
+// acc[D] first, then m and l.  Each lane moves its column's row; the same
+// agent-coherent accesses as the slots.
+template <int D, int NVC>
+__device__ __forceinline__ void row_store(float* base, int bytes, int64_t row, const State<NVC>& s, bool on) {
+    const int g = lane_id() >> 4;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRawBufferWord3);
+    if (!on) return;
+    const int off = int(row) * (D + 4) * 4;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r, off + (16 * c + 4 * g) * 4, 0,
+                                               kAgentCoherent);
+    if (g == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.m), r, off + D * 4, 0, kAgentCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.l), r, off + (D + 1) * 4, 0, kAgentCoherent);
+    }
+}
+
+template <int D, int NVC>
+__device__ __forceinline__ void row_load(const float* base, int bytes, int64_t row, State<NVC>& s, bool on) {
+    const int g = lane_id() >> 4;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, kRawBufferWord3);
+    const int off = on ? int(row) * (D + 4) * 4 : 0;  // lanes without a row read row 0 and never use it
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+        s.acc[c] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + (16 * c + 4 * g) * 4, 0, kAgentCoherent));
+    s.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + D * 4, 0, kAgentCoherent));
+    s.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + (D + 1) * 4, 0, kAgentCoherent));
+}
+
 // A wave's merged state of the partitions it has finished of the current run
 // waits in LDS (lane-major, conflict-free) while the next partition streams,
 // so it occupies no registers in the streaming loop.
@@ -245,13 +278,14 @@ __device__ __forceinline__ void lds_get(const LdsState<NVC>& x, State<NVC>& s) {
         for (int r = 0; r < 4; ++r) s.acc[c][r] = x.acc[4 * c + r][lane];
 }
 
-// out[s][head0 + col][:] = v_scale * acc / l (0 for a run without scores).
+// Output row `row` (sequence * num_heads + head) of this lane's column:
+// v_scale * acc / l (0 for a row without scores).
 template <int QT, int D, int NVC>
-__device__ __forceinline__ void state_output(const DecodeArgs& a, int s, int head0, const State<NVC>& st, bool hv) {
-    const int lane = lane_id(), g = lane >> 4, col = lane & 15;
+__device__ __forceinline__ void state_output(const DecodeArgs& a, int64_t row, const State<NVC>& st, bool hv) {
+    const int g = lane_id() >> 4;
     if (!hv) return;
     const float inv = st.l > 0.0f ? a.v_scale / st.l : 0.0f;
-    const int64_t o = (int64_t(s) * a.num_heads + head0 + col) * D + 4 * g;
+    const int64_t o = row * D + 4 * g;
 #pragma unroll
     for (int c = 0; c < NVC; ++c) {
         const f32x4 r = st.acc[c] * inv;
@@ -264,64 +298,150 @@ __device__ __forceinline__ void state_output(const DecodeArgs& a, int s, int hea
     }
 }
 
+// How sequence s is decoded.  Plain: its runs read blocks [0, nb).  Shared
+// prefix: its first pbe blocks are read by the prefix runs of sequence cl
+// (the first of the consecutive sequences of s's sharing group that one
+// prefix run serves), whose columns hold the heads of `members` sequences;
+// its own suffix runs read blocks [pbe, nb), and the two states are merged.
+// The test is made from s's and cl's entries alone, so every sequence is
+// covered by exactly one prefix run or by none, whatever the arrays hold.
+struct SeqInfo {
+    int len;  // clamped context length (0 past the batch)
+    int pbe;  // blocks read by a prefix run (0: plain)
+    int cl;   // sequence whose prefix runs cover s (-1: plain)
+};
+
+__device__ __forceinline__ int shared_blocks(const DecodeArgs& a, int s, int L) {
+    const int pb = a.prefix_blocks[s];
+    const int full = L / kBlockTokens;  // only whole blocks are shared
+    return pb < 0 ? 0 : (pb > full ? full : pb);
+}
+
+template <bool CAS>
+__device__ __forceinline__ SeqInfo seq_info(const DecodeArgs& a, int s) {
+    SeqInfo r{0, 0, -1};
+    if (s >= a.num_seqs) return r;
+    r.len = clamped_len(a, s);
+    if constexpr (CAS) {
+        const int pbs = shared_blocks(a, s, r.len);
+        const int ld = a.prefix_leader[s];
+        if (pbs > 0 && ld >= 0 && ld <= s) {
+            const int c = ld + (s - ld) / a.members * a.members;
+            const bool ok = c == s || (a.prefix_leader[c] == ld && shared_blocks(a, c, clamped_len(a, c)) == pbs);
+            if (ok) {
+                r.pbe = pbs;
+                r.cl = c;
+            }
+        }
+    }
+    return r;
+}
+
+// Units of sequence s: its suffix (or plain) runs, plus the prefix runs it leads.
+__device__ __forceinline__ uint32_t seq_units(const DecodeArgs& a, const SeqInfo& si, int s) {
+    const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
+    return uint32_t(nb - si.pbe + (si.cl == s ? si.pbe : 0)) * uint32_t(a.runs);
+}
+
 // Forward cursor over the sequences, 64 at a time: lane i holds sequence
-// base + i.  Units of a sequence = runs * blocks.
+// base + i.
 struct Cursor {
     int base;        // first sequence of the chunk
-    int len;         // lane: clamped context length (0 past the batch)
+    SeqInfo si;      // lane: its sequence
     uint32_t inc;    // lane: inclusive prefix of units over the chunk
     uint32_t start;  // units before the chunk
     uint32_t tot;    // units in the chunk
 };
 
+template <bool CAS>
 __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int base) {
     const int s = base + lane_id();
     c.base = base;
-    c.len = s < a.num_seqs ? clamped_len(a, s) : 0;
-    c.inc = wave_scan(uint32_t((c.len + kBlockTokens - 1) / kBlockTokens) * uint32_t(a.runs));
+    c.si = seq_info<CAS>(a, s);
+    c.inc = wave_scan(seq_units(a, c.si, s));
     c.tot = __builtin_amdgcn_readlane(c.inc, 63);
 }
 
+template <bool CAS>
 __device__ __forceinline__ void cursor_advance(Cursor& c, const DecodeArgs& a) {
     c.start += c.tot;
-    cursor_load(c, a, c.base + 64);
+    cursor_load<CAS>(c, a, c.base + 64);
 }
 
 // Lane of the chunk holding the sequence that contains unit u (u < U).
+template <bool CAS>
 __device__ __forceinline__ int cursor_find(Cursor& c, const DecodeArgs& a, uint32_t u) {
-    while (c.start + c.tot <= u) cursor_advance(c, a);
+    while (c.start + c.tot <= u) cursor_advance<CAS>(c, a);
     return __builtin_ctzll(__ballot(c.start + c.inc > u));
 }
 
-// Lane of the next non-empty sequence after lane i (one exists).
+// Lane of the next sequence with units after lane i (one exists).
+template <bool CAS>
 __device__ __forceinline__ int cursor_next(Cursor& c, const DecodeArgs& a, int i) {
-    unsigned long long m = __ballot(lane_id() > i && c.len > 0);
+    if constexpr (!CAS) {  // a sequence has units exactly when it has tokens
+        unsigned long long m = __ballot(lane_id() > i && c.si.len > 0);
+        while (m == 0) {
+            cursor_advance<CAS>(c, a);
+            m = __ballot(c.si.len > 0);
+        }
+        return __builtin_ctzll(m);
+    }
+    const uint32_t prev = __shfl_up(c.inc, 1);
+    unsigned long long m = __ballot(lane_id() > i && c.inc != (lane_id() == 0 ? 0u : prev));
     while (m == 0) {
-        cursor_advance(c, a);
-        m = __ballot(c.len > 0);
+        cursor_advance<CAS>(c, a);
+        const uint32_t p = __shfl_up(c.inc, 1);
+        m = __ballot(c.inc != (lane_id() == 0 ? 0u : p));
     }
     return __builtin_ctzll(m);
 }
 
-// One segment: the softmax state of run (s, hg) over its blocks [j0, j1).
+// Lane `lane`'s query / output row and column state for one run.
+struct Cols {
+    int64_t row;  // sequence * num_heads + head (a valid row for lanes without a head)
+    bool hv;      // the column holds a head
+    bool sne;     // prefix runs: that head's sequence also has suffix runs
+};
+
+// Columns of a plain or suffix run (s, hg): heads hg * rh + col, col < rh.
+__device__ __forceinline__ Cols plain_cols(const DecodeArgs& a, int s, int hg) {
+    const int col = lane_id() & 15;
+    const bool hv = col < a.rh;
+    return Cols{int64_t(s) * a.num_heads + hg * a.rh + (hv ? col : 0), hv, false};
+}
+
+// Columns of prefix run (s, hg): column col serves head hg * rh + col % rh of
+// sequence s + col / rh, if that sequence is covered by s's prefix runs.
+template <bool CAS>
+__device__ __forceinline__ Cols prefix_cols(const DecodeArgs& a, const Cursor& cur, int i, int s, int hg, int pbe) {
+    const int col = lane_id() & 15;
+    const int member = col / a.rh;
+    const int sm = s + member;
+    const int src = min(i + member, 63);
+    SeqInfo x{__shfl(cur.si.len, src), 0, __shfl(cur.si.cl, src)};
+    if (i + member >= 64) x = seq_info<CAS>(a, sm);  // in the next chunk of the cursor
+    const bool hv = col < a.members * a.rh && x.cl == s;
+    const bool sne = (x.len + kBlockTokens - 1) / kBlockTokens > pbe;
+    return Cols{int64_t(hv ? sm : s) * a.num_heads + hg * a.rh + col % a.rh, hv, sne};
+}
+
+// One segment: the softmax state of one run over blocks [j0, j1) of sequence
+// s's table, for KV head kvh; this lane's column holds query row `qr` if hv.
 template <int KV, int D, int P>
-__device__ void run_segment(const DecodeArgs& a, int s, int L, int hg, int j0, int j1, State<Geo<KV, D>::NVC>& st) {
+__device__ void run_segment(const DecodeArgs& a, int s, int L, int kvh, int64_t qr, bool hv, int j0, int j1,
+                            State<Geo<KV, D>::NVC>& st) {
     using GE = Geo<KV, D>;
     using T = Tile<KV, D>;
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
     const int lane = lane_id();
     const int g = lane >> 4;    // row group of the matrix-core operands
     const int col = lane & 15;  // head column (QK output, PV output) / token row (K operand)
-    const int head0 = hg * a.rh;
-    const int kvh = head0 / a.group;
-    const bool hv = col < a.rh;
 
     // ---- query operand: Q^T, heads on columns, zero for unused columns ----
     QOp<KV> qop[GE::NQ];
     {
         const int qelt = (QT == kF32) ? 4 : 2;
-        const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
-                              (int64_t(s) * a.num_heads + head0 + (hv ? col : 0)) * D * qelt;
+        const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * D * qelt;
         if constexpr (KV == kBF16) {
 #pragma unroll
             for (int u = 0; u < GE::NQ; ++u) {
@@ -534,9 +654,11 @@ __device__ __forceinline__ int peek_arrivals(const DecodeArgs& a, const Contrib&
     return seen;
 }
 
-template <int QT, int D, int NVC>
-__device__ void merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, int s, int head0,
-                             const State<NVC>& mine, LdsState<NVC>& own_state, bool hv, int seen) {
+// Returns true in the one wave that ends up with the run's whole state (left
+// in own_state).
+template <int D, int NVC>
+__device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, const State<NVC>& mine,
+                             LdsState<NVC>& own_state, bool hv, int seen) {
     auto slot = [&](uint32_t i) { return slot_ptr(a, c.w0 + i, (i == 0 && c.first_in_slot1) ? 1 : 0); };
     const int slot_bytes = a.slot_floats * 4;
     seen = __builtin_amdgcn_readfirstlane(seen);
@@ -563,7 +685,7 @@ __device__ void merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
                 old = __builtin_amdgcn_readfirstlane(old);
                 last = uint32_t(old) == members - 1;
             }
-            if (!last) return;  // a later arrival completes the group
+            if (!last) return false;  // a later arrival completes the group
             if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below are issued after the count was seen
             // members in index order, two states per round trip; this wave's own from LDS
@@ -598,9 +720,71 @@ __device__ void merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
         cnt = (cnt + kMergeFanIn - 1) / kMergeFanIn;
         span *= kMergeFanIn;
     }
-    State<NVC> out;
-    lds_get(own_state, out);
-    state_output<QT, D>(a, s, head0, out, hv);
+    return true;
+}
+
+// merge(prefix, suffix) for the meeting: the same rule as state_merge with
+// every product and sum rounded on its own (no fused multiply-add), so the
+// two places that compute it produce the same bits whichever side came last.
+template <int NVC>
+__device__ __forceinline__ void meet_merge(State<NVC>& p, const State<NVC>& t) {
+#pragma clang fp contract(off)
+    const float M = fmaxf(p.m, t.m);
+    const float wp = p.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(p.m - M);
+    const float wt = t.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(t.m - M);
+    p.m = M;
+    p.l = p.l * wp + t.l * wt;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) p.acc[c] = p.acc[c] * wp + t.acc[c] * wt;
+}
+
+// Shared-prefix meeting.  The output of a covered (sequence, head) row is
+// merge(prefix state, suffix state).  Each side stores its rows, then counts
+// itself in the (sequence, run) counter; the second arrival resets it, loads
+// the other side's rows and writes the output.  Both sides merge as
+// merge(prefix, suffix), so the result does not depend on which came second.
+template <int QT, int D, int NVC>
+__device__ void meet_suffix(const DecodeArgs& a, int s, int hg, const Cols& cm, const State<NVC>& st) {
+    row_store<D>(a.sstate, a.state_bytes, cm.row, st, cm.hv);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // the rows have reached the coherent level before they are counted
+    int* ctr = a.meet + int64_t(s) * a.runs + hg;
+    int old = 0;
+    if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == 0) return;  // the prefix rows come later
+    if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    State<NVC> p;
+    row_load<D>(a.pstate, a.state_bytes, cm.row, p, cm.hv);
+    meet_merge(p, st);
+    state_output<QT, D>(a, cm.row, p, cm.hv);
+}
+
+template <int QT, int D, int NVC>
+__device__ void meet_prefix(const DecodeArgs& a, int s, int hg, const Cols& cm, const State<NVC>& st) {
+    const int lane = lane_id(), col = lane & 15, g = lane >> 4;
+    const int member = col / a.rh;
+    const bool meet = cm.hv && cm.sne;  // rows whose sequence has suffix runs
+    row_store<D>(a.pstate, a.state_bytes, cm.row, st, meet);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    int old = 0;  // one arrival per member sequence, by its first column's lane of row group 0
+    if (g == 0 && meet && col == member * a.rh) {
+        int* ctr = a.meet + int64_t(s + member) * a.runs + hg;
+        old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = __shfl(old, member * a.rh);
+    const bool merge = meet && old == 1;    // the suffix rows are there
+    const bool direct = cm.hv && !cm.sne;   // no suffix: the prefix state is the whole state
+    if (!__ballot(merge || direct)) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    State<NVC> t;
+    row_load<D>(a.sstate, a.state_bytes, cm.row, t, merge);
+    State<NVC> res = st;
+    if (merge) meet_merge(res, t);
+    state_output<QT, D>(a, cm.row, res, merge || direct);
 }
 
 constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round trip
@@ -611,7 +795,7 @@ constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round t
 template <int KV, int D>
 constexpr int kWavesPerSimd = (KV == kF32 && D == 128) ? 1 : 2;
 
-template <int KV, int D, int P>
+template <int KV, int D, int P, bool CAS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D>))) void paged_decode_kernel(
     DecodeArgs a) {
     using GE = Geo<KV, D>;
@@ -620,7 +804,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     const uint32_t w = blockIdx.x;
     const uint32_t nwt = gridDim.x;
     const int lane = lane_id();
-    const bool hv = (lane & 15) < a.rh;
 
     // ---- total units; per-chunk totals of the first kLenChunks chunks; rows
     //      of empty sequences are zeroed (sequence s by wave s mod grid) ----
@@ -629,21 +812,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
 #pragma unroll
     for (int c = 0; c < kLenChunks; ++c) ctot[c] = 0;
     for (int base = 0; base < a.num_seqs; base += 64 * kLenChunks) {
-        int len[kLenChunks];
+        SeqInfo si[kLenChunks];
 #pragma unroll
-        for (int c = 0; c < kLenChunks; ++c) {
-            const int s = base + 64 * c + lane;
-            len[c] = s < a.num_seqs ? clamped_len(a, s) : 0;
-        }
+        for (int c = 0; c < kLenChunks; ++c) si[c] = seq_info<CAS>(a, base + 64 * c + lane);
 #pragma unroll
         for (int c = 0; c < kLenChunks; ++c) {
             const int cb = base + 64 * c;
             if (cb >= a.num_seqs) break;
-            const uint32_t units = uint32_t((len[c] + kBlockTokens - 1) / kBlockTokens) * uint32_t(a.runs);
-            const uint32_t t = __builtin_amdgcn_readlane(wave_scan(units), 63);
+            const uint32_t t = __builtin_amdgcn_readlane(wave_scan(seq_units(a, si[c], cb + lane)), 63);
             if (base == 0) ctot[c] = t;
             U += t;
-            unsigned long long empty = __ballot(cb + lane < a.num_seqs && len[c] == 0);
+            unsigned long long empty = __ballot(cb + lane < a.num_seqs && si[c].len == 0);
             while (empty) {
                 const int se = cb + __builtin_ctzll(empty);
                 empty &= empty - 1;
@@ -670,14 +849,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
     }
-    cursor_load(cur, a, 64 * chunk);
-    int i = cursor_find(cur, a, lo);
-    int L = __builtin_amdgcn_readlane(cur.len, i);
-    int nb = (L + kBlockTokens - 1) / kBlockTokens;
-    const uint32_t seq_first = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - uint32_t(nb * a.runs);
-    int hg = int((lo - seq_first) / uint32_t(nb));
-    int j = int((lo - seq_first) % uint32_t(nb));
-    uint32_t run_first = seq_first + uint32_t(hg * nb);
+    cursor_load<CAS>(cur, a, 64 * chunk);
+    int i = cursor_find<CAS>(cur, a, lo);
+    // Runs of a sequence: npre prefix runs over blocks [0, pbe) (when it leads
+    // a prefix group), then its runs over blocks [pbe, nb).
+    int L = 0, nb = 0, pbe = 0, npre = 0;
+    auto enter = [&]() {
+        L = __builtin_amdgcn_readlane(cur.si.len, i);
+        nb = (L + kBlockTokens - 1) / kBlockTokens;
+        if constexpr (CAS) {
+            pbe = __builtin_amdgcn_readlane(cur.si.pbe, i);
+            npre = __builtin_amdgcn_readlane(cur.si.cl, i) == cur.base + i ? a.runs : 0;
+        }
+    };
+    enter();
+    int r, j;
+    uint32_t run_first;
+    {
+        const uint32_t units = uint32_t(npre * pbe + (nb - pbe) * a.runs);
+        const uint32_t seq_first = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - units;
+        uint32_t o = lo - seq_first;
+        const uint32_t pre_units = uint32_t(npre * pbe);
+        if (o < pre_units) {
+            r = int(o / uint32_t(pbe));
+            j = int(o % uint32_t(pbe));
+            run_first = lo - uint32_t(j);
+        } else {
+            o -= pre_units;
+            const uint32_t sl = uint32_t(nb - pbe);
+            r = npre + int(o / sl);
+            j = pbe + int(o % sl);
+            run_first = lo - uint32_t(j - pbe);
+        }
+    }
 
     // ---- partitions: kk equal pieces of the stretch, each <= part_blocks ----
     const uint32_t len = hi - lo;
@@ -690,9 +894,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     uint32_t u = lo;
     while (true) {
         const int s = cur.base + i;
-        const uint32_t run_end = run_first + uint32_t(nb);
+        const bool pre = r < npre;
+        const int hg = pre ? r : r - npre;
+        const uint32_t run_end = run_first + uint32_t(pre ? pbe : nb - pbe);
         const uint32_t seg_end = run_end < cut ? run_end : cut;
         const int j1 = j + int(seg_end - u);
+        Cols cm = plain_cols(a, s, hg);
+        if constexpr (CAS) {
+            if (pre) cm = prefix_cols<CAS>(a, cur, i, s, hg, pbe);
+        }
         // this segment ends the wave's part of the run: the run is finished
         // here if it lies in the stretch, else it is merged with other waves
         const bool ends_part = seg_end == run_end || seg_end == hi;
@@ -704,7 +914,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             seen = peek_arrivals(a, cb, w);
         }
         State<NVC> st;
-        run_segment<KV, D, P>(a, s, L, hg, j, j1, st);
+        run_segment<KV, D, P>(a, s, pre ? pbe * kBlockTokens : L, hg * a.rh / a.group, cm.row, cm.hv, j, j1, st);
         if (holding) {  // earlier partitions first
             State<NVC> prev;
             lds_get(held, prev);
@@ -723,19 +933,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             continue;
         }
         holding = false;
-        if (local)
-            state_output<QT, D>(a, s, hg * a.rh, st, hv);
-        else
-            merge_across<QT, D>(a, cb, w, s, hg * a.rh, st, held, hv, seen);
-        if (u == hi) break;
-        j = 0;
-        run_first = run_end;
-        if (++hg == a.runs) {
-            hg = 0;
-            i = cursor_next(cur, a, i);
-            L = __builtin_amdgcn_readlane(cur.len, i);
-            nb = (L + kBlockTokens - 1) / kBlockTokens;
+        bool whole = local;
+        if (!local && merge_across<D>(a, cb, w, st, held, cm.hv, seen)) {
+            lds_get(held, st);
+            whole = true;
         }
+        if (whole) {
+            if constexpr (CAS) {
+                if (pre)
+                    meet_prefix<QT, D>(a, s, hg, cm, st);
+                else if (pbe > 0)
+                    meet_suffix<QT, D>(a, s, hg, cm, st);
+                else
+                    state_output<QT, D>(a, cm.row, st, cm.hv);
+            } else {
+                state_output<QT, D>(a, cm.row, st, cm.hv);
+            }
+        }
+        if (u == hi) break;
+        run_first = run_end;
+        if (++r == npre + (nb > pbe ? a.runs : 0)) {
+            i = cursor_next<CAS>(cur, a, i);
+            enter();
+            r = 0;
+        }
+        j = r < npre ? 0 : pbe;
     }
 }
 
@@ -764,10 +986,10 @@ int device_cus() {
     return cached;
 }
 
-template <int KV, int D>
+template <int KV, int D, bool CAS>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int P = Depth<KV, D>::P;
-    auto kern = paged_decode_kernel<KV, D, P>;
+    auto kern = paged_decode_kernel<KV, D, P, CAS>;
     static int waves_per_cu = 0;  // occupancy of this instance (64-thread workgroups)
     if (waves_per_cu == 0) {
         int n = 0;
@@ -785,15 +1007,21 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+template <bool CAS>
+hipError_t launch_c(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+    if (cache_dtype == kF32 && head_dim == 64) return launch_t<kF32, 64, CAS>(a, stream);
+    if (cache_dtype == kF32 && head_dim == 128) return launch_t<kF32, 128, CAS>(a, stream);
+    if (cache_dtype == kBF16 && head_dim == 64) return launch_t<kBF16, 64, CAS>(a, stream);
+    if (cache_dtype == kBF16 && head_dim == 128) return launch_t<kBF16, 128, CAS>(a, stream);
+    if (cache_dtype == kFP8 && head_dim == 64) return launch_t<kFP8, 64, CAS>(a, stream);
+    if (cache_dtype == kFP8 && head_dim == 128) return launch_t<kFP8, 128, CAS>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    if (cache_dtype == kF32 && head_dim == 64) return launch_t<kF32, 64>(a, stream);
-    if (cache_dtype == kF32 && head_dim == 128) return launch_t<kF32, 128>(a, stream);
-    if (cache_dtype == kBF16 && head_dim == 64) return launch_t<kBF16, 64>(a, stream);
-    if (cache_dtype == kBF16 && head_dim == 128) return launch_t<kBF16, 128>(a, stream);
-    if (cache_dtype == kFP8 && head_dim == 64) return launch_t<kFP8, 64>(a, stream);
-    if (cache_dtype == kFP8 && head_dim == 128) return launch_t<kFP8, 128>(a, stream);
-    return hipErrorInvalidValue;
+    return a.prefix_leader ? launch_c<true>(cache_dtype, head_dim, a, stream)
+                           : launch_c<false>(cache_dtype, head_dim, a, stream);
 }
 
 }  // namespace pkv

@@ -62,16 +62,23 @@ inline int run_heads(int group) {
 // completes leaves its counters at zero again):
 //   kWsHeader reserved words,
 //   kMergeLevels x kMaxWaves int32 arrival counters (one per merge group),
+//   kMeetCounters int32 arrival counters of the shared-prefix meeting (one per
+//   (sequence, run); zero and unused in plain decode),
 //   two partial-state slots per wave: slot 0 for the run a wave continues from
 //   the wave before it, slot 1 for the run it hands on to the waves after it.
-// Slot layout (floats): m[16], l[16], acc[run_heads][D].
+//   Slot layout (floats): m[16], l[16], acc[columns][D].
+// Every counter sits at the same place for every entry point and shape, so
+// one zero-filled buffer serves any sequence of calls; slots and state rows
+// hold data only and need no clearing.
 constexpr int kWsHeader = 16;
 constexpr int kMergeFanIn = 8;   // states one merge step combines
 constexpr int kMergeLevels = 4;  // kMergeFanIn^kMergeLevels >= kMaxWaves
+constexpr int kMeetCounters = 1 << 18;
 constexpr int kSlotHead = 2 * kMaxRunHeads;
-inline int64_t slot_floats(int rh, int head_dim) { return kSlotHead + int64_t(rh) * head_dim; }
-inline int64_t workspace_floats(int rh, int head_dim) {
-    return kWsHeader + int64_t(kMergeLevels) * kMaxWaves + 2 * int64_t(kMaxWaves) * slot_floats(rh, head_dim);
+constexpr int64_t kSlotBase = kWsHeader + int64_t(kMergeLevels) * kMaxWaves + kMeetCounters;
+inline int64_t slot_floats(int columns, int head_dim) { return kSlotHead + int64_t(columns) * head_dim; }
+inline int64_t workspace_floats(int columns, int head_dim) {
+    return kSlotBase + 2 * int64_t(kMaxWaves) * slot_floats(columns, head_dim);
 }
 
 struct DecodeArgs {
@@ -94,7 +101,21 @@ struct DecodeArgs {
     int32_t slot_floats; // floats per partial slot
     float score_scale;   // scale * k_scale * log2(e): scores are kept in base-2 units
     float v_scale;       // 1 for f32 / bf16 pools
+    // shared-prefix decode only (null / 0 otherwise)
+    const int32_t* prefix_leader;  // [num_seqs] first sequence of each sequence's sharing group
+    const int32_t* prefix_blocks;  // [num_seqs] leading blocks shared with that group
+    int32_t* meet;                 // [num_seqs * runs] arrival counters of prefix and suffix states (workspace)
+    float* pstate;                 // [num_seqs * num_heads] state rows of the prefix part
+    float* sstate;                 // [num_seqs * num_heads] state rows of the suffix part
+    int32_t members;               // sequences whose heads share one prefix run's columns
+    int32_t state_bytes;           // bytes of pstate (and of sstate)
 };
+
+// Shared-prefix state rows, after the slots: two arrays (prefix, suffix) of
+// num_seqs * num_heads rows (row = sequence * num_heads + head) of head_dim + 4
+// floats: acc[head_dim], m, l, two unused.
+inline int64_t align_floats(int64_t n) { return (n + 63) / 64 * 64; }
+inline int64_t state_row_floats(int head_dim) { return int64_t(head_dim) + 4; }
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 

@@ -87,6 +87,8 @@ class Workload:
     v_scale: float = 1.0
     partition_size: int = 0          # 0 = library default
     block_size: int = BLOCK_SIZE
+    prefix_leader: Optional[np.ndarray] = None  # [B] int32 first sequence of each sharing group
+    prefix_blocks: Optional[np.ndarray] = None  # [B] int32 leading blocks the group shares
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -348,7 +350,103 @@ def _make_prefix(seed: int, prompts: int = 32, samples: int = 8, prefix: int = 1
     return Workload(name="prefix", num_seqs=B, num_heads=hq, num_kv_heads=hkv, head_dim=d,
                     q_dtype="bf16", in_dtype="bf16", cache_dtype="bf16", context_lens=lens, q=q,
                     new_k=new_k, new_v=new_v, layout=shared, twin=twin,
-                    scale=float(np.float32(1.0) / np.sqrt(np.float32(d))))
+                    scale=float(np.float32(1.0) / np.sqrt(np.float32(d))),
+                    prefix_leader=(np.arange(B, dtype=np.int32) // samples * samples).astype(np.int32),
+                    prefix_blocks=np.full(B, pb, dtype=np.int32))
+
+
+def make_shared(name: str, seed: int, groups, num_heads: int, num_kv_heads: int, head_dim: int,
+                q_dtype: str, cache_dtype: str, in_dtype: Optional[str] = None, partition_size: int = 0,
+                spare_blocks: int = 3) -> Workload:
+    """Consecutive groups of sequences that share a prompt prefix (parallel samples of one prompt).
+
+    groups: list of (prefix_tokens, [length of each member]), every length >= prefix_tokens.  The
+    prefix_tokens // 16 whole blocks of a group's prefix are one set of physical blocks in every member's
+    table; a partly filled last prefix block is a private copy per member (what a copy-on-write leaves),
+    followed by the member's private tokens.  Each token value is drawn once: the prefix per group, the rest
+    per member.  The new token of a member is its last one; when that lies in a shared block (the member has
+    no private token), it is written with the prefix and the member's new slot is -1."""
+    if in_dtype is None:
+        in_dtype = q_dtype if cache_dtype == "fp8" else cache_dtype
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(0,))))
+    lens, leader, pblocks, gid, pre_len = [], [], [], [], []
+    for g, (pre, members) in enumerate(groups):
+        first = len(lens)
+        for L in members:
+            if L < pre:
+                raise ValueError("a member is shorter than its group's prefix")
+            lens.append(int(L)); leader.append(first); pblocks.append(pre // BLOCK_SIZE)
+            gid.append(g); pre_len.append(pre)
+    lens = np.asarray(lens, dtype=np.int32)
+    B = len(lens)
+    shared_n = [pre // BLOCK_SIZE for pre, _ in groups]
+    own_n = [blocks_for(L) - pblocks[s] for s, L in enumerate(lens.tolist())]
+    pool = sum(shared_n) + sum(own_n) + spare_blocks
+    perm = rng.permutation(pool).astype(np.int64)
+    k = 0
+    gblocks = []
+    for n in shared_n:
+        gblocks.append([int(b) for b in perm[k:k + n]]); k += n
+    lists = []
+    for s in range(B):
+        ids = list(gblocks[gid[s]]) + [int(b) for b in perm[k:k + own_n[s]]]
+        k += own_n[s]
+        lists.append(ids)
+    mb = max([len(x) for x in lists] + [1])
+    bt = _table_from_lists(lists, mb)
+
+    pre_tot = sum(pre for pre, _ in groups)
+    own_tot = int(sum(int(L) - pre_len[s] for s, L in enumerate(lens.tolist())))
+    pk = _values(seed, 2, (pre_tot, num_kv_heads, head_dim), in_dtype)
+    pv = _values(seed, 3, (pre_tot, num_kv_heads, head_dim), in_dtype)
+    ok_ = _values(seed, 4, (own_tot, num_kv_heads, head_dim), in_dtype)
+    ov_ = _values(seed, 5, (own_tot, num_kv_heads, head_dim), in_dtype)
+    pstart = np.concatenate([[0], np.cumsum([pre for pre, _ in groups])[:-1]]).astype(np.int64)
+    ostart = np.concatenate([[0], np.cumsum([int(L) - pre_len[s] for s, L in enumerate(lens.tolist())])[:-1]]
+                            ).astype(np.int64) if B else np.zeros(0, dtype=np.int64)
+
+    def token(s: int, t: int):
+        """K and V rows of position t of sequence s."""
+        if t < pre_len[s]:
+            i = pstart[gid[s]] + t
+            return pk[i], pv[i]
+        i = ostart[s] + t - pre_len[s]
+        return ok_[i], ov_[i]
+
+    hk, hv, hs = [], [], []
+    new_k = np.zeros((B, num_kv_heads, head_dim), dtype=pk.dtype)
+    new_v = np.zeros((B, num_kv_heads, head_dim), dtype=pv.dtype)
+    new_slots = np.full(B, -1, dtype=np.int32)
+    for s in range(B):
+        L = int(lens[s])
+        sh = pblocks[s] * BLOCK_SIZE
+        first_of_group = leader[s] == s
+        for t in range(L):
+            kt, vt = token(s, t)
+            slot = int(_slots_for(bt[s], np.array([t]))[0])
+            if t < sh:
+                if first_of_group:
+                    hk.append(kt); hv.append(vt); hs.append(slot)
+            elif t == L - 1:
+                new_k[s], new_v[s], new_slots[s] = kt, vt, slot
+            else:
+                hk.append(kt); hv.append(vt); hs.append(slot)
+        if L > 0 and L - 1 < sh:  # last token inside the shared prefix: written with the prefix
+            new_k[s], new_v[s] = token(s, L - 1)
+    shp = (0, num_kv_heads, head_dim)
+    hist = WriteBatch(np.ascontiguousarray(np.stack(hk)) if hk else np.zeros(shp, dtype=pk.dtype),
+                      np.ascontiguousarray(np.stack(hv)) if hv else np.zeros(shp, dtype=pv.dtype),
+                      np.asarray(hs, dtype=np.int32))
+    q = _values(seed, 1, (B, num_heads, head_dim), q_dtype)
+    w = Workload(name=name, num_seqs=B, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                 q_dtype=q_dtype, in_dtype=in_dtype, cache_dtype=cache_dtype, context_lens=lens, q=q,
+                 new_k=new_k, new_v=new_v, layout=Layout(pool, bt, [hist], new_slots),
+                 scale=float(np.float32(1.0) / np.sqrt(np.float32(head_dim))), partition_size=partition_size,
+                 prefix_leader=np.asarray(leader, dtype=np.int32), prefix_blocks=np.asarray(pblocks, dtype=np.int32))
+    if cache_dtype == "fp8":
+        w.k_scale = float(np.float32(_amax([pk, ok_], in_dtype)) / np.float32(448.0))
+        w.v_scale = float(np.float32(_amax([pv, ov_], in_dtype)) / np.float32(448.0))
+    return w
 
 
 def context_lengths(name: str, seed: Optional[int] = None) -> np.ndarray:

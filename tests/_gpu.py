@@ -107,3 +107,17 @@ def max_err(a: np.ndarray, b: np.ndarray):
     d = np.abs(a - b)
     i = int(np.argmax(d)) if d.size else 0
     return (float(d.reshape(-1)[i]) if d.size else 0.0), np.unravel_index(i, d.shape) if d.size else None
+
+
+def gpu_decode_cascade(w: W.Workload, layout: W.Layout, kp, vp, prefix_leader=None, prefix_blocks=None,
+                       partition_size=None, workspace=None):
+    q_dev = to_dev(w.q, w.q_dtype)
+    out = torch.empty_like(q_dev)
+    part = w.partition_size if partition_size is None else partition_size
+    pl = w.prefix_leader if prefix_leader is None else prefix_leader
+    pb = w.prefix_blocks if prefix_blocks is None else prefix_blocks
+    pkv.paged_attention_decode_cascade(out, q_dev, kp, vp, to_dev(layout.block_table, "i32"),
+                                       to_dev(w.context_lens, "i32"), to_dev(pl, "i32"), to_dev(pb, "i32"),
+                                       w.scale, w.k_scale, w.v_scale, partition_size=part, workspace=workspace)
+    torch.cuda.synchronize()
+    return widen(to_host(out, w.q_dtype), w.q_dtype)

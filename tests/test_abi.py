@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 4
+    assert lib.pkv_abi_version() == 5
     for st in range(7):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -104,9 +104,16 @@ def test_decode_validation(lib):
 
 
 def _ws(run_heads, d):
-    """Header (16 words) + 4 merge levels x 4096 arrival counters + two
+    """Header (16 words) + 4 merge levels x 4096 arrival counters + 2^18 shared-prefix meeting counters + two
     partial-state slots per persistent wave (4096 at most) of 32 + run_heads * D floats."""
-    return (16 + 4 * W + 2 * W * (32 + run_heads * d)) * 4
+    return (16 + 4 * W + (1 << 18) + 2 * W * (32 + run_heads * d)) * 4
+
+
+def _cws(b, hq, columns, d):
+    """The decode workspace with slots `columns` wide, then two arrays of b * hq state rows of d + 4 floats
+    (each rounded up to 64 floats)."""
+    rows = -(-(b * hq * (d + 4)) // 64) * 64
+    return _ws(columns, d) + 2 * rows * 4
 
 
 W = 4096                   # persistent waves (upper bound)
@@ -143,3 +150,32 @@ def test_check_inputs_validation(lib):
     assert _chk(lib, NB=1 << 27) == INVALID           # slots overflow int32
     assert _chk(lib, counts=A + 4) == ALIGN
     assert _chk(lib, cl=A + 2) == ALIGN
+
+
+def _cas(lib, **kw):
+    a = dict(out=A, q=A, qd=1, kc=A, vc=A, cd=1, bt=A, MB=64, cl=A, pl=A, pb=A, B=4, H=32, Hkv=8, D=128, bs=16,
+             NB=300, scale=0.088, ks=1.0, vs=1.0, part=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return lib.paged_attention_decode_cascade(a["out"], a["q"], a["qd"], a["kc"], a["vc"], a["cd"], a["bt"], a["MB"],
+                                              a["cl"], a["pl"], a["pb"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"],
+                                              a["NB"], a["scale"], a["ks"], a["vs"], a["part"], a["ws"], a["wsb"], None)
+
+
+def test_cascade_validation_and_workspace(lib):
+    cws = lib.paged_attention_cascade_workspace_bytes
+    assert cws(256, 32, 8, 128, 96, 16, 0) == _cws(256, 32, 16, 128)   # GQA 4: 4 sequences x 4 heads
+    assert cws(64, 40, 40, 128, 128, 16, 0) == _cws(64, 40, 16, 128)   # MHA: 16 sequences x 1 head
+    assert cws(16, 64, 8, 128, 2048, 16, 512) == _cws(16, 64, 16, 128)  # GQA 8: 2 x 8
+    assert cws(4, 24, 2, 64, 10, 16, 0) == _cws(4, 24, 12, 64)          # runs of 12: one sequence per run
+    assert cws(2, 8, 3, 64, 10, 16, 0) == 0
+    assert cws(2, 8, 8, 64, 10, 16, 24) == 0
+    assert _cas(lib, pl=0) == INVALID
+    assert _cas(lib, pb=0) == INVALID
+    assert _cas(lib, pl=A + 2) == ALIGN
+    assert _cas(lib, B=-1) == INVALID
+    assert _cas(lib, D=96) == UNSUPPORTED
+    assert _cas(lib, B=(1 << 18) // 8 + 1, MB=4) == UNSUPPORTED       # more (sequence, run) pairs than counters
+    need = cws(4, 32, 8, 128, 64, 16, 0)
+    assert _cas(lib, wsb=need - 1) == WORKSPACE
+    assert _cas(lib, wsb=lib.paged_attention_workspace_bytes(4, 32, 8, 128, 64, 16, 0)) == WORKSPACE
+    assert _cas(lib, B=0) == OK

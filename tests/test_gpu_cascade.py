@@ -1,0 +1,147 @@
+"""GPU parity of the shared-prefix (cascade) decode.
+
+paged_attention_decode_cascade must give attention over each sequence's own
+table: the oracle's result within the decode tolerances (1e-5 fp32, 2e-2
+bf16, 6e-2 fp8 pools), and the plain GPU decode's result within the same
+bound.  With no sharing declared it is the plain decode bit for bit; a
+repeat call gives the same bits; the workspace's counters are zero again
+after every call; sharing entries that disagree with their chunk only make
+a sequence decode on its own, so the result stays right.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_369_amd as pkv
+from paged_kv_cache_369_amd import workloads as W
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+COUNTERS = (64, 64 + (4 * 4096 + (1 << 18)) * 4)  # byte range of every arrival counter in a workspace
+
+# groups of (prefix tokens, member lengths): block-aligned and ragged prefixes, members with no private
+# token, a member-less-than-a-chunk group, a group of 19 (ragged last chunk), an unshared sequence
+GROUPS = [(256, [300, 257, 272, 512, 260]), (100, [100, 130, 101]), (64, [64, 64, 80]), (0, [50]),
+          (512, [600, 513, 530, 700, 1000, 520, 515, 640, 512, 900, 610, 777, 530, 545, 600, 560, 999, 514, 700]),
+          (1024, [1024 + 16 * i + 1 for i in range(6)])]
+
+
+def _check(w, got, layout=None, tol=None):
+    layout = layout or w.layout
+    ok, ov = _gpu.oracle_pools(w, layout)
+    want = _gpu.oracle_decode(w, layout, ok, ov)
+    err, where = _gpu.max_err(got, want)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    assert err <= (tol or _gpu.TOL[w.cache_dtype]), (err, where)
+
+
+@pytest.mark.parametrize("hq,hkv,d,cache", [
+    (32, 8, 128, "bf16"),   # GQA 4: four sequences per prefix run
+    (8, 8, 128, "bf16"),    # one query head per KV head: sixteen sequences per prefix run
+    (64, 8, 128, "fp8"),    # GQA 8: two sequences per prefix run
+    (8, 8, 64, "f32"),
+    (24, 2, 64, "bf16"),    # runs of 12 heads: one sequence per prefix run
+    (32, 1, 128, "bf16"),   # two runs per KV head
+    (16, 2, 64, "fp8"),
+])
+@pytest.mark.parametrize("part", [0, 64])
+def test_cascade_parity(gpu, hq, hkv, d, cache, part):
+    qd = "f32" if cache == "f32" else "bf16"
+    w = W.make_shared("cascade", 40 + hq + d, GROUPS, hq, hkv, d, qd, cache, partition_size=part)
+    _gpu.note(f"cascade parity hq={hq} hkv={hkv} d={d} cache={cache} part={part}")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp)
+    plain = _gpu.gpu_decode(w, w.layout, kp, vp)
+    assert np.max(np.abs(got - plain)) <= _gpu.TOL[cache]
+    again = _gpu.gpu_decode_cascade(w, w.layout, kp, vp)
+    assert np.array_equal(got, again)
+    _check(w, got)
+
+
+def test_prefix_workload_scaled(gpu):
+    """The shared-prefix workload's shape (8 samples per prompt, 32/8 heads, bf16) at reduced size."""
+    w = W.make_scaled("prefix", 24)
+    _gpu.note("cascade prefix workload scaled")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp)
+    plain = _gpu.gpu_decode(w, w.layout, kp, vp)
+    assert np.max(np.abs(got - plain)) <= _gpu.TOL["bf16"]
+    _check(w, got)
+
+
+def test_no_sharing_is_plain_decode_bit_exact(gpu):
+    w = W.make_shared("cascade0", 9, GROUPS, 32, 8, 128, "bf16", "bf16")
+    _gpu.note("cascade with no sharing declared")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    zeros = np.zeros(w.num_seqs, dtype=np.int32)
+    for part in (0, 64):
+        got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp, prefix_blocks=zeros, partition_size=part)
+        plain = _gpu.gpu_decode(w, w.layout, kp, vp, partition_size=part)
+        assert np.array_equal(got, plain)
+
+
+def test_disagreeing_entries_decode_on_their_own(gpu):
+    """Leaders after the sequence, negative leaders, a shorter shared length, a length past the context and a
+    leader inside the group that is not its first: such sequences are decoded on their own (or share less),
+    and since every block they claim to share really is shared, the result is still attention over their
+    tables."""
+    w = W.make_shared("cascadebad", 17, GROUPS, 32, 8, 128, "bf16", "bf16")
+    pl = w.prefix_leader.copy()
+    pb = w.prefix_blocks.copy()
+    pl[1] = 3            # a leader after the sequence
+    pl[2] = -4
+    pb[3] = 2            # shares fewer blocks than its chunk says
+    pb[6] = 1 << 20      # past its context: clamped to its whole blocks, then disagrees with its chunk
+    pl[14] = 13          # a leader inside the group that is not its first
+    pb[9] = 0
+    _gpu.note("cascade with disagreeing sharing entries")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    ws = torch.zeros(pkv.paged_attention_cascade_workspace_bytes(w.num_seqs, 32, 8, 128, w.max_blocks_per_seq),
+                     dtype=torch.uint8, device="cuda")
+    got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp, prefix_leader=pl, prefix_blocks=pb, workspace=ws)
+    _check(w, got)
+    assert int(torch.count_nonzero(ws[COUNTERS[0]:COUNTERS[1]])) == 0
+
+
+def test_workspace_shared_with_plain_calls(gpu):
+    """One zero-filled workspace serves plain and cascade calls of different shapes in turn; every counter
+    is zero after each call and the outputs do not change."""
+    wa = W.make_shared("cascA", 21, GROUPS, 32, 8, 128, "bf16", "bf16")
+    wb = W.make_shared("cascB", 22, GROUPS[:3], 8, 8, 64, "f32", "f32")
+    need = max(pkv.paged_attention_cascade_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                                           w.max_blocks_per_seq) for w in (wa, wb))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    pools = {}
+    for w in (wa, wb):
+        pools[w.name] = _gpu.gpu_pools(w, w.layout)
+    first = {}
+    for rep in range(2):
+        for w in (wa, wb):
+            kp, vp = pools[w.name]
+            _gpu.note(f"shared workspace rep={rep} {w.name}")
+            q = _gpu.to_dev(w.q, w.q_dtype)
+            out = torch.empty_like(q)
+            pkv.paged_attention_decode(out, q, kp, vp, _gpu.to_dev(w.layout.block_table, "i32"),
+                                       _gpu.to_dev(w.context_lens, "i32"), w.scale, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws[COUNTERS[0]:COUNTERS[1]])) == 0
+            got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp, workspace=ws)
+            assert int(torch.count_nonzero(ws[COUNTERS[0]:COUNTERS[1]])) == 0
+            if rep == 0:
+                first[w.name] = got
+                _check(w, got)
+            else:
+                assert np.array_equal(first[w.name], got)
+
+
+def test_long_shared_prefix_merge_tree(gpu):
+    """A 40000-token prefix shared by 6 samples beside short sequences: the prefix runs are cut over hundreds
+    of waves (tree merge), then meet their samples' suffix runs."""
+    groups = [(40000, [40000 + 7 * i + 1 for i in range(6)]), (0, [5]), (3000, [3001, 3100]), (0, [1])]
+    w = W.make_shared("casclong", 33, groups, 32, 8, 128, "bf16", "bf16")
+    _gpu.note("cascade long prefix")
+    kp, vp = _gpu.gpu_pools(w, w.layout)
+    for part in (0, 512):
+        got = _gpu.gpu_decode_cascade(w, w.layout, kp, vp, partition_size=part)
+        _check(w, got)
