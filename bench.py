@@ -90,6 +90,32 @@ def load_traffic(workload: str):
     return int(t["bytes_per_call"]), os.path.relpath(path, ROOT)
 
 
+def run_heads(group: int) -> int:
+    """Query heads one decode run serves: the largest divisor of the GQA group that is at most 16."""
+    for g in range(min(group, 16), 1, -1):
+        if group % g == 0:
+            return g
+    return 1
+
+
+def cascade_read_bytes(w) -> int:
+    """KV bytes the shared-prefix decode reads for a workload with consistent sharing arrays: each chunk of
+    16 / run_heads consecutive group members reads the group's shared tokens once, and every sequence reads
+    its own tokens after them."""
+    members = 16 // run_heads(w.num_heads // w.num_kv_heads)
+    tokens = 0
+    for s, L in enumerate(w.context_lens.tolist()):
+        pb = min(max(int(w.prefix_blocks[s]), 0), L // 16)
+        if pb > 0 and (s - int(w.prefix_leader[s])) % members == 0:
+            tokens += pb * 16
+        tokens += L - pb * 16
+    return tokens * w.num_kv_heads * w.head_dim * 2 * w.kv_elt_bytes()
+
+
+def profile_key(args) -> str:
+    return args.workload + ("-cascade" if args.cascade else "")
+
+
 def _dev(a, dtype, torch):
     a = np.ascontiguousarray(a)
     if dtype == "bf16":
@@ -173,6 +199,8 @@ def _pick(per_kernel, key):
 
 
 # Longest context each workload's length law allows: what a contiguous allocator must reserve per sequence.
+CASCADE_NOTE = ", decoded by paged_attention_decode_cascade (each shared prefix read once per chunk of samples)"
+
 MAX_LEN = {"tiny": 100, "13b": 2048, "gqa8b": 8192, "prefix": 1024 + 512, "longfp8": 32768}
 
 
@@ -235,8 +263,9 @@ def summarize_counters(args) -> int:
         raise SystemExit("no paged_decode_kernel rows in the counter runs")
     mean = {k: sum(v) / len(v) for k, v in vals.items()}
     from paged_kv_cache_369_amd import workloads as W
-    lines = [f"# SQ counters of `paged_decode_kernel`, workload `{args.workload}`", "",
-             WORKLOAD_DESC[args.workload], "", "Commands (run from the repository root):", ""]
+    lines = [f"# SQ counters of `paged_decode_kernel`, workload `{profile_key(args)}`", "",
+             WORKLOAD_DESC[args.workload] + (CASCADE_NOTE if args.cascade else ""), "",
+             "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in args.commands]
     lines += ["", "Mean over the profiled dispatches (each counter summed over the device by rocprofv3).", "",
               "| counter | value per dispatch |", "|---|---|"]
@@ -262,7 +291,7 @@ def summarize_counters(args) -> int:
         lines += ["", "Ratios:", ""] + derived
     lines += ["", f"Decode source digest `{decode_source_digest()}`."]
     os.makedirs(args.out_dir, exist_ok=True)
-    path = os.path.join(args.out_dir, f"paged_decode_{args.workload}_sq_counters.md")
+    path = os.path.join(args.out_dir, f"paged_decode_{profile_key(args)}_sq_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
@@ -287,20 +316,21 @@ def summarize_traffic(args) -> int:
     total = sum(k["fetch_bytes"] + k["write_bytes"] for k in kernels.values())
     from paged_kv_cache_369_amd import workloads as W
     w = W.make(args.workload)
-    kv = w.kv_bytes()
-    rec = {"workload": args.workload, "source_digest": decode_source_digest(),
+    kv = cascade_read_bytes(w) if args.cascade else w.kv_bytes()
+    rec = {"workload": profile_key(args), "source_digest": decode_source_digest(),
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                                 "fetch_scale": fscale, "write_scale": wscale},
            "kernels": kernels, "bytes_per_call": int(round(total)), "algorithmic_kv_bytes": kv,
            "commands": args.commands}
     os.makedirs(args.out_dir, exist_ok=True)
-    with open(traffic_file(args.workload, args.out_dir), "w") as f:
+    with open(traffic_file(profile_key(args), args.out_dir), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = traffic_file(args.workload, args.out_dir).replace(".json", ".md")
+    md = traffic_file(profile_key(args), args.out_dir).replace(".json", ".md")
     with open(md, "w") as f:
-        f.write(f"# HBM traffic of one decode call, workload `{args.workload}`\n\n")
-        f.write(f"{WORKLOAD_DESC[args.workload]}.\n\nCommands (run from the repository root):\n\n")
+        f.write(f"# HBM traffic of one decode call, workload `{profile_key(args)}`\n\n")
+        f.write(f"{WORKLOAD_DESC[args.workload]}{CASCADE_NOTE if args.cascade else ''}.\n\n"
+                "Commands (run from the repository root):\n\n")
         for c in args.commands:
             f.write(f"    {c}\n")
         f.write("\nCounter scale from the plain 1 GiB device copy (`__amd_rocclr_copyBuffer`): "
@@ -358,6 +388,8 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-oracle baseline and check (-1 = all, 0 = skip)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode with paged_attention_decode_cascade using the workload's sharing arrays")
     ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
                     help="read (or overwrite) 512 MB before every step, outside the timed brackets, so the step's "
                          "KV reads cannot hit what the previous step left in the 256 MB infinity cache")
@@ -408,6 +440,9 @@ def main() -> int:
         f"sum(L)={int(w.context_lens.sum())} blocks={w.layout.num_blocks}")
     part = w.partition_size if args.partition_size < 0 else args.partition_size
     layout = w.layout
+    if args.cascade and w.prefix_leader is None:
+        print(f"workload {args.workload} declares no shared prefixes", file=sys.stderr)
+        return 2
 
     # device-resident inputs
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
@@ -425,8 +460,12 @@ def main() -> int:
     out = torch.empty_like(q)
     bt = _dev(layout.block_table, "i32", torch)
     cl = _dev(w.context_lens, "i32", torch)
-    ws_bytes = pkv.paged_attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
-                                                   w.max_blocks_per_seq, W.BLOCK_SIZE, part)
+    ws_query = pkv.paged_attention_cascade_workspace_bytes if args.cascade else pkv.paged_attention_workspace_bytes
+    ws_bytes = ws_query(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq, W.BLOCK_SIZE,
+                        part)
+    if args.cascade:
+        pl = _dev(w.prefix_leader, "i32", torch)
+        pbl = _dev(w.prefix_blocks, "i32", torch)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
@@ -434,8 +473,12 @@ def main() -> int:
         pkv.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
 
     def decode():
-        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale, partition_size=part,
-                                   workspace=ws)
+        if args.cascade:
+            pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, pl, pbl, w.scale, w.k_scale, w.v_scale,
+                                               partition_size=part, workspace=ws)
+        else:
+            pkv.paged_attention_decode(out, q, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
+                                       partition_size=part, workspace=ws)
 
     for _ in range(args.warmup):
         write()
@@ -472,13 +515,13 @@ def main() -> int:
     t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     dec_us = float(np.mean(t_dec))
-    kv_bytes = w.kv_bytes()
+    kv_bytes = cascade_read_bytes(w) if args.cascade else w.kv_bytes()
     achieved = kv_bytes / (dec_us * 1e-6) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; events: write {np.mean(t_write):.1f} us, "
         f"decode call {dec_us:.1f} us (p10 {np.percentile(t_dec, 10):.1f}, p90 {np.percentile(t_dec, 90):.1f}), "
         f"KV {kv_bytes / 1e9:.3f} GB -> {achieved:.0f} GB/s")
 
-    traffic, traffic_src = load_traffic(args.workload)
+    traffic, traffic_src = load_traffic(profile_key(args))
     overhead = {"q_bytes": q.numel() * q.element_size(), "out_bytes": out.numel() * out.element_size(),
                 "block_table_bytes": bt.numel() * 4, "context_lens_bytes": cl.numel() * 4}
     result = {
@@ -499,7 +542,8 @@ def main() -> int:
                    "block_size": W.BLOCK_SIZE, "kv_dtype": w.cache_dtype, "q_dtype": w.q_dtype,
                    "sum_context": int(w.context_lens.sum()),
                    "partition_size": part, "kv_bytes": kv_bytes, "kv_unique_bytes": w.kv_unique_bytes(),
-                   "mall_flush": args.flush_mall},
+                   "kv_logical_bytes": w.kv_bytes(), "mall_flush": args.flush_mall,
+                   "decode": "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
