@@ -267,6 +267,24 @@ __device__ __forceinline__ void lds_put(LdsState<NVC>& x, const State<NVC>& s) {
         for (int r = 0; r < 4; ++r) x.acc[4 * c + r][lane] = s.acc[c][r];
 }
 
+// s <- merge(x, s) with x read from LDS one accumulator at a time (the
+// earlier state first, as state_merge(x, s) would compute it).
+template <int NVC>
+__device__ __forceinline__ void lds_merge_into(const LdsState<NVC>& x, State<NVC>& s) {
+    const int lane = lane_id();
+    const float xm = x.m[lane];
+    const float M = fmaxf(xm, s.m);
+    const float wx = xm == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(xm - M);
+    const float ws = s.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s.m - M);
+    s.m = M;
+    s.l = x.l[lane] * wx + s.l * ws;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) {
+        const f32x4 xa = {x.acc[4 * c][lane], x.acc[4 * c + 1][lane], x.acc[4 * c + 2][lane], x.acc[4 * c + 3][lane]};
+        s.acc[c] = xa * wx + s.acc[c] * ws;
+    }
+}
+
 template <int NVC>
 __device__ __forceinline__ void lds_get(const LdsState<NVC>& x, State<NVC>& s) {
     const int lane = lane_id();
@@ -425,193 +443,170 @@ __device__ __forceinline__ Cols prefix_cols(const DecodeArgs& a, const Cursor& c
     return Cols{int64_t(hv ? sm : s) * a.num_heads + hg * a.rh + col % a.rh, hv, sne};
 }
 
-// One segment: the softmax state of one run over blocks [j0, j1) of sequence
-// s's table, for KV head kvh; this lane's column holds query row `qr` if hv.
-template <int KV, int D, int P>
-__device__ void run_segment(const DecodeArgs& a, int s, int L, int kvh, int64_t qr, bool hv, int j0, int j1,
-                            State<Geo<KV, D>::NVC>& st) {
+// ---- the per-block steps, shared by every run kind ----
+
+// Query operand Q^T of one run: this lane's column holds query row `qr` (heads
+// on columns; zero for columns without a head).
+template <int KV, int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int64_t qr, bool hv, QOp<KV> (&qop)[Geo<KV, D>::NQ]) {
     using GE = Geo<KV, D>;
-    using T = Tile<KV, D>;
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
-    const int lane = lane_id();
-    const int g = lane >> 4;    // row group of the matrix-core operands
-    const int col = lane & 15;  // head column (QK output, PV output) / token row (K operand)
-
-    // ---- query operand: Q^T, heads on columns, zero for unused columns ----
-    QOp<KV> qop[GE::NQ];
-    {
-        const int qelt = (QT == kF32) ? 4 : 2;
-        const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * D * qelt;
-        if constexpr (KV == kBF16) {
+    const int g = lane_id() >> 4;
+    const int qelt = (QT == kF32) ? 4 : 2;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * D * qelt;
+    if constexpr (KV == kBF16) {
 #pragma unroll
-            for (int u = 0; u < GE::NQ; ++u) {
-                const uint4 x = hv ? *reinterpret_cast<const uint4*>(qrow + (32 * u + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
-                qop[u] = __builtin_bit_cast(bf16x8, x);
+        for (int u = 0; u < GE::NQ; ++u) {
+            const uint4 x = hv ? *reinterpret_cast<const uint4*>(qrow + (32 * u + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
+            qop[u] = __builtin_bit_cast(bf16x8, x);
+        }
+    } else if constexpr (KV == kFP8) {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint4 x =
+                    hv ? *reinterpret_cast<const uint4*>(qrow + (64 * u + 16 * g + 8 * e) * 2) : make_uint4(0, 0, 0, 0);
+                qop[2 * u + e] = __builtin_bit_cast(bf16x8, x);
             }
-        } else if constexpr (KV == kFP8) {
+    } else {
 #pragma unroll
-            for (int u = 0; u < GE::NKL; ++u)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const uint4 x = hv ? *reinterpret_cast<const uint4*>(qrow + (64 * u + 16 * g + 8 * e) * 2)
-                                       : make_uint4(0, 0, 0, 0);
-                    qop[2 * u + e] = __builtin_bit_cast(bf16x8, x);
-                }
-        } else {
-#pragma unroll
-            for (int u = 0; u < GE::NKL; ++u) {
-                const float4 x = hv ? *reinterpret_cast<const float4*>(qrow + (16 * u + 4 * g) * 4)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-                qop[4 * u + 0] = x.x;
-                qop[4 * u + 1] = x.y;
-                qop[4 * u + 2] = x.z;
-                qop[4 * u + 3] = x.w;
-            }
+        for (int u = 0; u < GE::NKL; ++u) {
+            const float4 x =
+                hv ? *reinterpret_cast<const float4*>(qrow + (16 * u + 4 * g) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            qop[4 * u + 0] = x.x;
+            qop[4 * u + 1] = x.y;
+            qop[4 * u + 2] = x.z;
+            qop[4 * u + 3] = x.w;
         }
     }
+}
 
-    const int32_t* bt_row = a.block_table + int64_t(s) * a.max_blocks;
-    const int64_t block_stride = int64_t(a.num_kv_heads) * GE::TILE;
-    const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + int64_t(kvh) * GE::TILE + lane * 16;
-    const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + int64_t(kvh) * GE::TILE +
-                           (col * kBlockTokens + 4 * g) * GE::ELT;
+// Step 1: the K and V tiles of physical block `id`, KV head kvh.
+template <int KV, int D>
+__device__ __forceinline__ void load_tile(const DecodeArgs& a, int kvh, int id, Tile<KV, D>& t) {
+    using GE = Geo<KV, D>;
+    const int lane = lane_id(), g = lane >> 4, col = lane & 15;
+    const int64_t off = (int64_t(id) * a.num_kv_heads + kvh) * GE::TILE;
+    const uint8_t* kt = static_cast<const uint8_t*>(a.k_cache) + off + lane * 16;
+    const uint8_t* vt = static_cast<const uint8_t*>(a.v_cache) + off + (col * kBlockTokens + 4 * g) * GE::ELT;
+#pragma unroll
+    for (int u = 0; u < GE::NKL; ++u) t.k[u] = *reinterpret_cast<const uint4*>(kt + u * 1024);
+#pragma unroll
+    for (int c = 0; c < GE::NVC; ++c) t.v[c] = *reinterpret_cast<const VLoad<KV>*>(vt + c * 16 * kBlockTokens * GE::ELT);
+}
 
-    // block ids, 64 per vector register: idc covers [j0 + 64 cq, +64), idn the next 64
-    auto load_ids = [&](int grp) -> int {
-        const int j = j0 + grp * 64 + lane;
-        return j < j1 ? bt_row[j] : -1;
-    };
-    int cq = 0;
-    int idc = load_ids(0);
-    int idn = load_ids(1);
+// Running softmax state of one run inside the streaming loop, in the
+// matrix-core output layout (see State); lsum is this lane's share of the
+// normaliser (its four rows), summed over the row groups when the state closes.
+template <int NVC>
+struct Run {
+    float m, lsum;
+    f32x4 acc[NVC];
+};
 
-    T buf[P];
-    int nvb[P];  // valid tokens of the buffered block (0: the block contributes nothing)
-    auto issue = [&](T& t, int& nv, int ji) {
-        const int jj = ji - j0;
-        if ((jj >> 6) != cq) {
-            idc = idn;
-            ++cq;
-            idn = load_ids(cq + 1);
-        }
-        int id = __builtin_amdgcn_readlane(idc, jj & 63);
-        const bool ok = id >= 0 && id < a.num_blocks;
-        nv = ok ? min(kBlockTokens, L - ji * kBlockTokens) : 0;
-        id = ok ? id : 0;
-        const uint8_t* kt = kbase + int64_t(id) * block_stride;
-        const uint8_t* vt = vbase + int64_t(id) * block_stride;
+template <int NVC>
+__device__ __forceinline__ void run_reset(Run<NVC>& r) {
+    r.m = kNegInf;
+    r.lsum = 0.0f;
 #pragma unroll
-        for (int u = 0; u < GE::NKL; ++u) t.k[u] = *reinterpret_cast<const uint4*>(kt + u * 1024);
-#pragma unroll
-        for (int c = 0; c < GE::NVC; ++c)
-            t.v[c] = *reinterpret_cast<const VLoad<KV>*>(vt + c * 16 * kBlockTokens * GE::ELT);
-    };
+    for (int c = 0; c < NVC; ++c) r.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
-    float m = kNegInf;  // running maximum of head `col` (base-2 units)
-    float lsum = 0.0f;  // this lane's share of the running normaliser of head `col`
-    f32x4 acc[GE::NVC];
-#pragma unroll
-    for (int c = 0; c < GE::NVC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto consume = [&](const T& t, int nv) {
-        // 2. scores: sacc[r] = S^T[token 4g + r][head col]
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KV == kBF16) {
-#pragma unroll
-            for (int u = 0; u < GE::NKL; ++u)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[u], sacc, 0, 0, 0);
-        } else if constexpr (KV == kFP8) {
-#pragma unroll
-            for (int u = 0; u < GE::NKL; ++u) {
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].x, t.k[u].y), qop[2 * u], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].z, t.k[u].w), qop[2 * u + 1], sacc, 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < GE::NKL; ++u) {
-                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[4 * u + 0], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[4 * u + 1], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[4 * u + 2], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[4 * u + 3], sacc, 0, 0, 0);
-            }
-        }
-        // 3. online softmax for head `col`
-        const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
-        float sv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[r] = r < cnt ? sacc[r] * a.score_scale : kNegInf;
-        float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        const bool live = mn != kNegInf;
-        const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-        m = mn;
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = live ? __builtin_amdgcn_exp2f(sv[r] - mn) : 0.0f;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-            for (int c = 0; c < GE::NVC; ++c) acc[c] *= alpha;
-        }
-        // 4. O^T += V^T P^T
-        if constexpr (KV == kF32) {
-            lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-            for (int c = 0; c < GE::NVC; ++c) {
-                const uint4 vv = t.v[c];
-                const float v0 = cnt > 0 ? __uint_as_float(vv.x) : 0.0f;
-                const float v1 = cnt > 1 ? __uint_as_float(vv.y) : 0.0f;
-                const float v2 = cnt > 2 ? __uint_as_float(vv.z) : 0.0f;
-                const float v3 = cnt > 3 ? __uint_as_float(vv.w) : 0.0f;
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, p[0], acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, p[1], acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, p[2], acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, p[3], acc[c], 0, 0, 0);
-            }
-        } else {
-            const uint32_t p01 = pack_bf16(p[0], p[1]);
-            const uint32_t p23 = pack_bf16(p[2], p[3]);
-            // the normaliser sums the rounded weights the products use
-            lsum = lsum * alpha + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                                   (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
-            const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
-            // keep-masks for this lane's four tokens (16 bits per bf16 token)
-            const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
-            const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-            for (int c = 0; c < GE::NVC; ++c) {
-                uint2 vv;
-                if constexpr (KV == kBF16) {
-                    vv = t.v[c];
-                } else {
-                    vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[c]), fp8x2_to_bf16x2<true>(t.v[c]));
-                }
-                vv.x &= mlo;
-                vv.y &= mhi;
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vv), pb, acc[c], 0, 0, 0);
-            }
-        }
-    };
-
-    // ---- software pipeline, P blocks deep ----
-#pragma unroll
-    for (int i = 0; i < P - 1; ++i) issue(buf[i], nvb[i], min(j0 + i, j1 - 1));
-    for (int jb = j0; jb < j1; jb += P) {
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            issue(buf[(i + P - 1) % P], nvb[(i + P - 1) % P], min(jb + i + P - 1, j1 - 1));
-            if (jb + i < j1) consume(buf[i], nvb[i]);
-        }
-    }
-
-    // ---- segment state: normaliser summed over the four row groups ----
-    float lt = lsum + __shfl_xor(lsum, 16);
+template <int NVC>
+__device__ __forceinline__ void run_close(const Run<NVC>& r, State<NVC>& st) {
+    float lt = r.lsum + __shfl_xor(r.lsum, 16);
     lt += __shfl_xor(lt, 32);
-    st.m = m;
+    st.m = r.m;
     st.l = lt;
 #pragma unroll
-    for (int c = 0; c < GE::NVC; ++c) st.acc[c] = acc[c];
+    for (int c = 0; c < NVC; ++c) st.acc[c] = r.acc[c];
+}
+
+// Steps 2-4 for one block with nv valid tokens.
+template <int KV, int D>
+__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv,
+                                             const QOp<KV> (&qop)[Geo<KV, D>::NQ], Run<Geo<KV, D>::NVC>& rs) {
+    using GE = Geo<KV, D>;
+    const int g = lane_id() >> 4;
+    // 2. scores: sacc[r] = S^T[token 4g + r][head col]
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV == kBF16) {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[u], sacc, 0, 0, 0);
+    } else if constexpr (KV == kFP8) {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].x, t.k[u].y), qop[2 * u], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].z, t.k[u].w), qop[2 * u + 1], sacc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[4 * u + 0], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[4 * u + 1], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[4 * u + 2], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[4 * u + 3], sacc, 0, 0, 0);
+        }
+    }
+    // 3. online softmax for head `col`
+    const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = r < cnt ? sacc[r] * a.score_scale : kNegInf;
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(rs.m, bm);
+    const bool live = mn != kNegInf;
+    const float alpha = live ? __builtin_amdgcn_exp2f(rs.m - mn) : 1.0f;
+    rs.m = mn;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = live ? __builtin_amdgcn_exp2f(sv[r] - mn) : 0.0f;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < GE::NVC; ++c) rs.acc[c] *= alpha;
+    }
+    // 4. O^T += V^T P^T
+    if constexpr (KV == kF32) {
+        rs.lsum = rs.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+        for (int c = 0; c < GE::NVC; ++c) {
+            const uint4 vv = t.v[c];
+            const float v0 = cnt > 0 ? __uint_as_float(vv.x) : 0.0f;
+            const float v1 = cnt > 1 ? __uint_as_float(vv.y) : 0.0f;
+            const float v2 = cnt > 2 ? __uint_as_float(vv.z) : 0.0f;
+            const float v3 = cnt > 3 ? __uint_as_float(vv.w) : 0.0f;
+            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, p[0], rs.acc[c], 0, 0, 0);
+            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, p[1], rs.acc[c], 0, 0, 0);
+            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, p[2], rs.acc[c], 0, 0, 0);
+            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, p[3], rs.acc[c], 0, 0, 0);
+        }
+    } else {
+        const uint32_t p01 = pack_bf16(p[0], p[1]);
+        const uint32_t p23 = pack_bf16(p[2], p[3]);
+        // the normaliser sums the rounded weights the products use
+        rs.lsum = rs.lsum * alpha + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+        const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+        // keep-masks for this lane's four tokens (16 bits per bf16 token)
+        const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
+        const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int c = 0; c < GE::NVC; ++c) {
+            uint2 vv;
+            if constexpr (KV == kBF16) {
+                vv = t.v[c];
+            } else {
+                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[c]), fp8x2_to_bf16x2<true>(t.v[c]));
+            }
+            vv.x &= mlo;
+            vv.y &= mhi;
+            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vv), pb, rs.acc[c], 0, 0, 0);
+        }
+    }
 }
 
 // Stretch geometry, identical in every wave: nw waves, wave w owns units
@@ -688,30 +683,20 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
             if (!last) return false;  // a later arrival completes the group
             if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below are issued after the count was seen
-            // members in index order, two states per round trip; this wave's own from LDS
+            // members in index order, one state per round trip; this wave's own from LDS
             const uint32_t own = idx - first;
             State<NVC> res;
             state_clear(res);
 #pragma unroll 1
-            for (uint32_t r = 0; r < members; r += 2) {
-                State<NVC> in[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint32_t k = min(r + t, members - 1);
-                    state_load<D>(slot((first + k) * span), slot_bytes, in[t], hv);
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint32_t k = r + t;
-                    if (k < members) {
-                        if (k == own) {
-                            State<NVC> o;
-                            lds_get(own_state, o);
-                            state_merge(res, o);
-                        } else {
-                            state_merge(res, in[t]);
-                        }
-                    }
+            for (uint32_t k = 0; k < members; ++k) {
+                if (k == own) {
+                    State<NVC> o;
+                    lds_get(own_state, o);
+                    state_merge(res, o);
+                } else {
+                    State<NVC> in;
+                    state_load<D>(slot((first + k) * span), slot_bytes, in, hv);
+                    state_merge(res, in);
                 }
             }
             lds_put(own_state, res);
@@ -762,7 +747,7 @@ __device__ void meet_suffix(const DecodeArgs& a, int s, int hg, const Cols& cm, 
 }
 
 template <int QT, int D, int NVC>
-__device__ void meet_prefix(const DecodeArgs& a, int s, int hg, const Cols& cm, const State<NVC>& st) {
+__device__ void meet_prefix(const DecodeArgs& a, int s, int hg, const Cols& cm, State<NVC>& st) {
     const int lane = lane_id(), col = lane & 15, g = lane >> 4;
     const int member = col / a.rh;
     const bool meet = cm.hv && cm.sne;  // rows whose sequence has suffix runs
@@ -782,12 +767,48 @@ __device__ void meet_prefix(const DecodeArgs& a, int s, int hg, const Cols& cm, 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     State<NVC> t;
     row_load<D>(a.sstate, a.state_bytes, cm.row, t, merge);
-    State<NVC> res = st;
-    if (merge) meet_merge(res, t);
-    state_output<QT, D>(a, cm.row, res, merge || direct);
+    if (merge) meet_merge(st, t);
+    state_output<QT, D>(a, cm.row, st, merge || direct);
 }
 
 constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round trip
+
+// A piece: consecutive units of one run inside one partition of a wave's
+// stretch, at most 64 blocks, so that its block ids fit in one vector
+// register.  The walker plans pieces a few ahead of the tile being consumed.
+enum PieceFlags : int {
+    kNewRun = 1,    // the first piece of a run in this wave: new query operand
+    kNewState = 2,  // starts a softmax state (a new run, or after a partition boundary)
+    kClose = 4,     // the state ends with this piece
+    kEndsPart = 8,  // ... and so does this wave's part of the run
+    kLocal = 16,    // the whole run lies in this wave's stretch
+};
+
+struct Piece {
+    uint32_t u0, u1;  // units [u0, u1) (u0 == u1: no piece)
+    int s;            // sequence whose table row holds the blocks
+    int L;            // tokens the run's blocks hold
+    int j0;           // logical block of unit u0
+    int info;         // head group (bits 0-15) | kind << 16 (0 plain, 1 prefix, 2 suffix) | flags << 20
+    uint32_t run_first, run_end;  // the run's units
+    uint32_t cols;    // bit c: column c holds a head; bit 16 + c: its sequence has suffix runs (prefix runs)
+    int ids;          // lane l < u1 - u0: physical block of logical block j0 + l
+};
+
+__device__ __forceinline__ int piece_hg(const Piece& p) { return p.info & 0xffff; }
+__device__ __forceinline__ int piece_kind(const Piece& p) { return (p.info >> 16) & 3; }
+__device__ __forceinline__ int piece_flags(const Piece& p) { return p.info >> 20; }
+
+// This lane's column of the piece's run (see Cols).
+__device__ __forceinline__ Cols piece_cols(const DecodeArgs& a, const Piece& p) {
+    const int col = lane_id() & 15;
+    const bool hv = (p.cols >> col) & 1u;
+    const bool sne = (p.cols >> (16 + col)) & 1u;
+    const int hg = piece_hg(p);
+    if (piece_kind(p) == 1)
+        return Cols{int64_t(p.s + (hv ? col / a.rh : 0)) * a.num_heads + hg * a.rh + col % a.rh, hv, sne};
+    return Cols{int64_t(p.s) * a.num_heads + hg * a.rh + (hv ? col : 0), hv, sne};
+}
 
 // Waves per SIMD the register allocation must allow: two for the 16-bit and
 // 8-bit pools (the streaming loop fits in 256 registers), one for fp32 pools
@@ -886,78 +907,186 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     // ---- partitions: kk equal pieces of the stretch, each <= part_blocks ----
     const uint32_t len = hi - lo;
     const uint32_t kk = a.part_blocks > 0 ? (len + uint32_t(a.part_blocks) - 1) / uint32_t(a.part_blocks) : 1u;
-    uint32_t piece = 1;
+    uint32_t part = 1;
     uint32_t cut = lo + uint32_t(uint64_t(len) / kk);
 
-    __shared__ LdsState<NVC> held;  // merged state of the current run's finished partitions
-    bool holding = false;
-    uint32_t u = lo;
-    while (true) {
+    // ---- pieces, planned in order: the walker's next piece of the stretch ----
+    uint32_t u = lo;     // first unit not yet planned
+    bool fresh = true;   // the next piece starts a new softmax state
+    auto plan = [&](Piece& pc) {
+        if (u >= hi) {
+            pc.u0 = pc.u1 = hi;
+            pc.info = 0;
+            pc.cols = 0;
+            pc.ids = -1;
+            return;
+        }
         const int s = cur.base + i;
         const bool pre = r < npre;
         const int hg = pre ? r : r - npre;
         const uint32_t run_end = run_first + uint32_t(pre ? pbe : nb - pbe);
         const uint32_t seg_end = run_end < cut ? run_end : cut;
-        const int j1 = j + int(seg_end - u);
-        Cols cm = plain_cols(a, s, hg);
+        const uint32_t pe = seg_end < u + 64u ? seg_end : u + 64u;
+        const bool close = pe == seg_end;
+        int f = 0;
+        if (u == run_first || u == lo) f |= kNewRun | kNewState;
+        if (fresh) f |= kNewState;
+        if (close) f |= kClose;
+        if (close && (seg_end == run_end || seg_end == hi)) f |= kEndsPart;
+        if (run_first >= lo && pe == run_end) f |= kLocal;
+        pc.u0 = u;
+        pc.u1 = pe;
+        pc.s = s;
+        pc.L = pre ? pbe * kBlockTokens : L;
+        pc.j0 = j;
+        pc.info = hg | ((pre ? 1 : (pbe > 0 ? 2 : 0)) << 16) | (f << 20);
+        pc.run_first = run_first;
+        pc.run_end = run_end;
+        pc.cols = (1u << a.rh) - 1u;
         if constexpr (CAS) {
-            if (pre) cm = prefix_cols<CAS>(a, cur, i, s, hg, pbe);
-        }
-        // this segment ends the wave's part of the run: the run is finished
-        // here if it lies in the stretch, else it is merged with other waves
-        const bool ends_part = seg_end == run_end || seg_end == hi;
-        const bool local = run_first >= lo && seg_end == run_end;
-        Contrib cb{0, 0, false};
-        int seen = -1;
-        if (ends_part && !local) {
-            cb = contributors(sp, run_first, run_end - 1);
-            seen = peek_arrivals(a, cb, w);
-        }
-        State<NVC> st;
-        run_segment<KV, D, P>(a, s, pre ? pbe * kBlockTokens : L, hg * a.rh / a.group, cm.row, cm.hv, j, j1, st);
-        if (holding) {  // earlier partitions first
-            State<NVC> prev;
-            lds_get(held, prev);
-            state_merge(prev, st);
-            st = prev;
-        }
-        u = seg_end;
-        if (u == cut && u < hi) {
-            ++piece;
-            cut = lo + uint32_t(uint64_t(piece) * len / kk);
-        }
-        if (!ends_part) {
-            lds_put(held, st);  // a partition boundary inside the run
-            holding = true;
-            j = j1;
-            continue;
-        }
-        holding = false;
-        bool whole = local;
-        if (!local && merge_across<D>(a, cb, w, st, held, cm.hv, seen)) {
-            lds_get(held, st);
-            whole = true;
-        }
-        if (whole) {
-            if constexpr (CAS) {
-                if (pre)
-                    meet_prefix<QT, D>(a, s, hg, cm, st);
-                else if (pbe > 0)
-                    meet_suffix<QT, D>(a, s, hg, cm, st);
-                else
-                    state_output<QT, D>(a, cm.row, st, cm.hv);
-            } else {
-                state_output<QT, D>(a, cm.row, st, cm.hv);
+            if (pre) {
+                const Cols x = prefix_cols<CAS>(a, cur, i, s, hg, pbe);
+                const uint32_t hvm = uint32_t(__ballot(x.hv)) & 0xffffu;  // row group 0 holds every column
+                const uint32_t snem = uint32_t(__ballot(x.hv && x.sne)) & 0xffffu;
+                pc.cols = hvm | (snem << 16);
             }
         }
-        if (u == hi) break;
-        run_first = run_end;
-        if (++r == npre + (nb > pbe ? a.runs : 0)) {
-            i = cursor_next<CAS>(cur, a, i);
-            enter();
-            r = 0;
+        pc.ids = lane < int(pe - u) ? a.block_table[int64_t(s) * a.max_blocks + j + lane] : -1;
+        // advance the walker past the piece
+        j += int(pe - u);
+        u = pe;
+        fresh = close;
+        if (u == cut && u < hi) {
+            ++part;
+            cut = lo + uint32_t(uint64_t(part) * len / kk);
         }
-        j = r < npre ? 0 : pbe;
+        if (close && seg_end == run_end && u < hi) {  // the next run
+            run_first = run_end;
+            if (++r == npre + (nb > pbe ? a.runs : 0)) {
+                i = cursor_next<CAS>(cur, a, i);
+                enter();
+                r = 0;
+            }
+            j = r < npre ? 0 : pbe;
+        }
+    };
+
+    // Slot 0 holds the piece being consumed; the tile P - 1 ahead lies in one
+    // of slots 0..P-1 (a slot is planned when the piece before it is
+    // consumed, so its block ids are loading while that piece's last tiles
+    // are consumed).
+    constexpr int NS = P;
+    Piece sl[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) plan(sl[k]);
+
+    using T = Tile<KV, D>;
+    QOp<KV> qop[GE::NQ], qn[GE::NQ];  // the query operand of slot 0's run, and of slot 1's
+    {
+        const Cols c0 = piece_cols(a, sl[0]);
+        load_q<KV, D>(a, c0.row, c0.hv, qop);
+        const Cols c1 = piece_cols(a, sl[1]);
+        load_q<KV, D>(a, c1.row, c1.hv, qn);
+    }
+    Run<NVC> rs;
+    run_reset(rs);
+
+    // the tile of unit ua: its piece's block id and valid tokens (a unit past
+    // the stretch loads block 0 of KV head 0 and counts no tokens)
+    auto issue = [&](T& tb, int& nv, uint32_t ua) {
+        int id = 0, kvh = 0, lim = 0;
+        bool real = false;
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            if (!real && ua < sl[k].u1) {
+                const int off = int(ua - sl[k].u0);
+                id = __builtin_amdgcn_readlane(sl[k].ids, off);
+                kvh = piece_hg(sl[k]) * a.rh / a.group;
+                lim = sl[k].L - (sl[k].j0 + off) * kBlockTokens;
+                real = true;
+            }
+        }
+        const bool ok = real && id >= 0 && id < a.num_blocks;
+        nv = ok ? min(kBlockTokens, lim) : 0;
+        load_tile<KV, D>(a, ok ? kvh : 0, ok ? id : 0, tb);
+    };
+
+    __shared__ LdsState<NVC> held;  // merged state of the current run's finished partitions
+    bool holding = false;
+    int seen = -1;  // arrivals seen before the last piece of a cut run (see peek_arrivals)
+    auto peek = [&]() {
+        seen = -1;
+        const int f = piece_flags(sl[0]);
+        if ((f & kEndsPart) && !(f & kLocal))
+            seen = peek_arrivals(a, contributors(sp, sl[0].run_first, sl[0].run_end - 1), w);
+    };
+    peek();
+
+    // the piece in slot 0 is consumed: close its state as flagged, then move
+    // the slots up, plan the next piece and load what it needs
+    auto next_piece = [&]() {
+        const int f = piece_flags(sl[0]);
+        if (f & kClose) {
+            const Cols cm = piece_cols(a, sl[0]);
+            State<NVC> st;
+            run_close(rs, st);
+            if (holding) lds_merge_into(held, st);  // earlier partitions first
+            if (!(f & kEndsPart)) {
+                lds_put(held, st);  // a partition boundary inside the run
+                holding = true;
+            } else {
+                holding = false;
+                bool whole = (f & kLocal) != 0;
+                if (!whole &&
+                    merge_across<D>(a, contributors(sp, sl[0].run_first, sl[0].run_end - 1), w, st, held, cm.hv,
+                                    seen)) {
+                    lds_get(held, st);
+                    whole = true;
+                }
+                if (whole) {
+                    if constexpr (CAS) {
+                        if (piece_kind(sl[0]) == 1)
+                            meet_prefix<QT, D>(a, sl[0].s, piece_hg(sl[0]), cm, st);
+                        else if (piece_kind(sl[0]) == 2)
+                            meet_suffix<QT, D>(a, sl[0].s, piece_hg(sl[0]), cm, st);
+                        else
+                            state_output<QT, D>(a, cm.row, st, cm.hv);
+                    } else {
+                        state_output<QT, D>(a, cm.row, st, cm.hv);
+                    }
+                }
+            }
+            run_reset(rs);  // a closed state is always followed by a new one
+        }
+        if (piece_flags(sl[1]) & kNewRun) {
+#pragma unroll
+            for (int q = 0; q < GE::NQ; ++q) qop[q] = qn[q];
+        }
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k) sl[k] = sl[k + 1];
+        plan(sl[NS - 1]);
+        if (piece_flags(sl[1]) & kNewRun) {
+            const Cols c1 = piece_cols(a, sl[1]);
+            load_q<KV, D>(a, c1.row, c1.hv, qn);
+        }
+        peek();
+    };
+
+    // ---- the tile stream: consume unit lo + t while unit lo + t + P - 1 loads ----
+    T buf[P];
+    int nvb[P];  // valid tokens of the buffered block (0: the block contributes nothing)
+#pragma unroll
+    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], lo + uint32_t(k));
+    for (uint32_t t = lo; t < hi; t += P) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const uint32_t ut = t + uint32_t(k);
+            if (ut < hi) {
+                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], ut + uint32_t(P - 1));
+                consume_tile<KV, D>(a, buf[k], nvb[k], qop, rs);
+                if (ut + 1 == sl[0].u1) next_piece();
+            }
+        }
     }
 }
 
