@@ -166,7 +166,7 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
         a.prefix_leader = prefix_leader;
         a.prefix_blocks = prefix_blocks;
         a.members = members;
-        a.meet = reinterpret_cast<int32_t*>(a.ws + pkv::kWsHeader + int64_t(pkv::kMergeLevels) * pkv::kMaxWaves);
+        a.meet = reinterpret_cast<int32_t*>(a.ws + pkv::kMeetBase);
         a.pstate = a.ws + base;
         a.sstate = a.pstate + pkv::align_floats(int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim));
         a.state_bytes = int32_t(state_bytes);

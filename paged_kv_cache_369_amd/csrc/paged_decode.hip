@@ -633,7 +633,8 @@ struct Contrib {
 };
 
 __device__ __forceinline__ Contrib contributors(const Split& sp, uint32_t run_first, uint32_t run_last) {
-    return Contrib{sp.wave_of(run_first), sp.wave_of(run_last), run_first != sp.lo(sp.wave_of(run_first))};
+    const uint32_t w0 = sp.wave_of(run_first);
+    return Contrib{w0, sp.wave_of(run_last), run_first != sp.lo(w0)};
 }
 
 // Arrivals already counted in this wave's first merge group, read while the
@@ -785,15 +786,24 @@ enum PieceFlags : int {
 };
 
 struct Piece {
-    uint32_t u0, u1;  // units [u0, u1) (u0 == u1: no piece)
+    uint32_t p0, p1;  // positions [p0, p1) of its tiles in the wave's stream (p0 == p1: no piece)
     int s;            // sequence whose table row holds the blocks
-    int L;            // tokens the run's blocks hold
-    int j0;           // logical block of unit u0
+    int lim0;         // tokens of the run at and after the piece's first block
     int info;         // head group (bits 0-15) | kind << 16 (0 plain, 1 prefix, 2 suffix) | flags << 20
-    uint32_t run_first, run_end;  // the run's units
+    uint32_t contrib; // a cut run's waves: w0 | (w1 << 13) | first_in_slot1 << 26
     uint32_t cols;    // bit c: column c holds a head; bit 16 + c: its sequence has suffix runs (prefix runs)
-    int ids;          // lane l < u1 - u0: physical block of logical block j0 + l
+    int ids;          // lane l < p1 - p0: physical block of the piece's l-th block
 };
+
+static_assert(kMaxWaves <= (1 << 13), "wave indices are packed in 13 bits");
+
+__device__ __forceinline__ uint32_t pack_contrib(const Contrib& c) {
+    return c.w0 | (c.w1 << 13) | (c.first_in_slot1 ? 1u << 26 : 0u);
+}
+
+__device__ __forceinline__ Contrib unpack_contrib(uint32_t v) {
+    return Contrib{v & 0x1fffu, (v >> 13) & 0x1fffu, ((v >> 26) & 1u) != 0};
+}
 
 __device__ __forceinline__ int piece_hg(const Piece& p) { return p.info & 0xffff; }
 __device__ __forceinline__ int piece_kind(const Piece& p) { return (p.info >> 16) & 3; }
@@ -813,8 +823,13 @@ __device__ __forceinline__ Cols piece_cols(const DecodeArgs& a, const Piece& p) 
 // Waves per SIMD the register allocation must allow: two for the 16-bit and
 // 8-bit pools (the streaming loop fits in 256 registers), one for fp32 pools
 // of head_dim 128, whose tiles are twice as large.
+#ifdef PKV_WAVES_PER_SIMD
+template <int KV, int D>
+constexpr int kWavesPerSimd = PKV_WAVES_PER_SIMD;
+#else
 template <int KV, int D>
 constexpr int kWavesPerSimd = (KV == kF32 && D == 128) ? 1 : 2;
+#endif
 
 template <int KV, int D, int P, bool CAS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D>))) void paged_decode_kernel(
@@ -871,7 +886,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
     }
     cursor_load<CAS>(cur, a, 64 * chunk);
-    int i = cursor_find<CAS>(cur, a, lo);
+    int i = 0;
     // Runs of a sequence: npre prefix runs over blocks [0, pbe) (when it leads
     // a prefix group), then its runs over blocks [pbe, nb).
     int L = 0, nb = 0, pbe = 0, npre = 0;
@@ -883,39 +898,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             npre = __builtin_amdgcn_readlane(cur.si.cl, i) == cur.base + i ? a.runs : 0;
         }
     };
-    enter();
-    int r, j;
-    uint32_t run_first;
-    {
+    int r = 0, j = 0;
+    uint32_t run_first = 0;
+    uint32_t len = 0, kk = 1, part = 1, cut = 0;
+    uint32_t u = 0;      // first unit not yet planned
+    bool fresh = true;   // the next piece starts a new softmax state
+    // position the walker at unit `at` (the start of the stretch)
+    auto seek = [&](uint32_t at) {
+        i = cursor_find<CAS>(cur, a, at);
+        enter();
         const uint32_t units = uint32_t(npre * pbe + (nb - pbe) * a.runs);
         const uint32_t seq_first = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - units;
-        uint32_t o = lo - seq_first;
+        uint32_t o = at - seq_first;
         const uint32_t pre_units = uint32_t(npre * pbe);
         if (o < pre_units) {
             r = int(o / uint32_t(pbe));
             j = int(o % uint32_t(pbe));
-            run_first = lo - uint32_t(j);
+            run_first = at - uint32_t(j);
         } else {
             o -= pre_units;
             const uint32_t sl = uint32_t(nb - pbe);
             r = npre + int(o / sl);
             j = pbe + int(o % sl);
-            run_first = lo - uint32_t(j - pbe);
+            run_first = at - uint32_t(j - pbe);
         }
-    }
+        // partitions: kk equal parts of the stretch, each <= part_blocks
+        len = hi - lo;
+        kk = a.part_blocks > 0 ? (len + uint32_t(a.part_blocks) - 1) / uint32_t(a.part_blocks) : 1u;
+        part = 1;
+        cut = lo + uint32_t(uint64_t(len) / kk);
+        u = at;
+        fresh = true;
+    };
+    seek(lo);
 
-    // ---- partitions: kk equal pieces of the stretch, each <= part_blocks ----
-    const uint32_t len = hi - lo;
-    const uint32_t kk = a.part_blocks > 0 ? (len + uint32_t(a.part_blocks) - 1) / uint32_t(a.part_blocks) : 1u;
-    uint32_t part = 1;
-    uint32_t cut = lo + uint32_t(uint64_t(len) / kk);
-
-    // ---- pieces, planned in order: the walker's next piece of the stretch ----
-    uint32_t u = lo;     // first unit not yet planned
-    bool fresh = true;   // the next piece starts a new softmax state
+    // ---- pieces, planned in order: the walker's next piece of the stream ----
+    uint32_t spos = 0;  // stream position (tiles planned so far)
     auto plan = [&](Piece& pc) {
         if (u >= hi) {
-            pc.u0 = pc.u1 = hi;
+            pc.p0 = pc.p1 = spos;
             pc.info = 0;
             pc.cols = 0;
             pc.ids = -1;
@@ -934,14 +955,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         if (close) f |= kClose;
         if (close && (seg_end == run_end || seg_end == hi)) f |= kEndsPart;
         if (run_first >= lo && pe == run_end) f |= kLocal;
-        pc.u0 = u;
-        pc.u1 = pe;
+        pc.p0 = spos;
+        pc.p1 = spos + (pe - u);
         pc.s = s;
-        pc.L = pre ? pbe * kBlockTokens : L;
-        pc.j0 = j;
+        pc.lim0 = (pre ? pbe * kBlockTokens : L) - j * kBlockTokens;
         pc.info = hg | ((pre ? 1 : (pbe > 0 ? 2 : 0)) << 16) | (f << 20);
-        pc.run_first = run_first;
-        pc.run_end = run_end;
+        pc.contrib = (f & kEndsPart) && !(f & kLocal) ? pack_contrib(contributors(sp, run_first, run_end - 1)) : 0u;
         pc.cols = (1u << a.rh) - 1u;
         if constexpr (CAS) {
             if (pre) {
@@ -953,6 +972,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
         pc.ids = lane < int(pe - u) ? a.block_table[int64_t(s) * a.max_blocks + j + lane] : -1;
         // advance the walker past the piece
+        spos = pc.p1;
         j += int(pe - u);
         u = pe;
         fresh = close;
@@ -991,18 +1011,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     Run<NVC> rs;
     run_reset(rs);
 
-    // the tile of unit ua: its piece's block id and valid tokens (a unit past
-    // the stretch loads block 0 of KV head 0 and counts no tokens)
-    auto issue = [&](T& tb, int& nv, uint32_t ua) {
+    // the tile at stream position pos: its piece's block id and valid tokens
+    // (a position past the stream loads block 0 of KV head 0 and counts no tokens)
+    auto issue = [&](T& tb, int& nv, uint32_t pos) {
         int id = 0, kvh = 0, lim = 0;
         bool real = false;
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            if (!real && ua < sl[k].u1) {
-                const int off = int(ua - sl[k].u0);
+            if (!real && pos < sl[k].p1) {
+                const int off = int(pos - sl[k].p0);
                 id = __builtin_amdgcn_readlane(sl[k].ids, off);
                 kvh = piece_hg(sl[k]) * a.rh / a.group;
-                lim = sl[k].L - (sl[k].j0 + off) * kBlockTokens;
+                lim = sl[k].lim0 - off * kBlockTokens;
                 real = true;
             }
         }
@@ -1018,7 +1038,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         seen = -1;
         const int f = piece_flags(sl[0]);
         if ((f & kEndsPart) && !(f & kLocal))
-            seen = peek_arrivals(a, contributors(sp, sl[0].run_first, sl[0].run_end - 1), w);
+            seen = peek_arrivals(a, unpack_contrib(sl[0].contrib), w);
     };
     peek();
 
@@ -1038,8 +1058,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 holding = false;
                 bool whole = (f & kLocal) != 0;
                 if (!whole &&
-                    merge_across<D>(a, contributors(sp, sl[0].run_first, sl[0].run_end - 1), w, st, held, cm.hv,
-                                    seen)) {
+                    merge_across<D>(a, unpack_contrib(sl[0].contrib), w, st, held, cm.hv, seen)) {
                     lds_get(held, st);
                     whole = true;
                 }
@@ -1072,19 +1091,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         peek();
     };
 
-    // ---- the tile stream: consume unit lo + t while unit lo + t + P - 1 loads ----
+    // ---- the tile stream: consume position t while position t + P - 1 loads ----
     T buf[P];
     int nvb[P];  // valid tokens of the buffered block (0: the block contributes nothing)
 #pragma unroll
-    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], lo + uint32_t(k));
-    for (uint32_t t = lo; t < hi; t += P) {
+    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], uint32_t(k));
+    bool more = true;
+    for (uint32_t t = 0; more; t += P) {
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            const uint32_t ut = t + uint32_t(k);
-            if (ut < hi) {
-                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], ut + uint32_t(P - 1));
+            const uint32_t tp = t + uint32_t(k);
+            more = more && tp < sl[0].p1;
+            if (more) {
+                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], tp + uint32_t(P - 1));
                 consume_tile<KV, D>(a, buf[k], nvb[k], qop, rs);
-                if (ut + 1 == sl[0].u1) next_piece();
+                if (tp + 1 == sl[0].p1) next_piece();
             }
         }
     }

@@ -60,13 +60,13 @@ inline int run_heads(int group) {
 
 // Workspace (caller-owned, zero-filled before its first use; every call that
 // completes leaves its counters at zero again):
-//   kWsHeader reserved words,
-//   kMergeLevels x kMaxWaves int32 arrival counters (one per merge group),
+//   kWsHeader reserved words;
+//   kMergeLevels x kMaxWaves int32 arrival counters (one per merge group);
 //   kMeetCounters int32 arrival counters of the shared-prefix meeting (one per
-//   (sequence, run); zero and unused in plain decode),
-//   two partial-state slots per wave: slot 0 for the run a wave continues from
-//   the wave before it, slot 1 for the run it hands on to the waves after it.
-//   Slot layout (floats): m[16], l[16], acc[columns][D].
+//   (sequence, run); zero and unused in plain decode);
+//   two partial-state slots per wave: slot 0 for the run the wave continues
+//   from the wave before it, slot 1 for the run it hands on to the waves
+//   after it.  Slot layout (floats): m[16], l[16], acc[columns][D].
 // Every counter sits at the same place for every entry point and shape, so
 // one zero-filled buffer serves any sequence of calls; slots and state rows
 // hold data only and need no clearing.
@@ -75,7 +75,8 @@ constexpr int kMergeFanIn = 8;   // states one merge step combines
 constexpr int kMergeLevels = 4;  // kMergeFanIn^kMergeLevels >= kMaxWaves
 constexpr int kMeetCounters = 1 << 18;
 constexpr int kSlotHead = 2 * kMaxRunHeads;
-constexpr int64_t kSlotBase = kWsHeader + int64_t(kMergeLevels) * kMaxWaves + kMeetCounters;
+constexpr int64_t kMeetBase = kWsHeader + int64_t(kMergeLevels) * kMaxWaves;
+constexpr int64_t kSlotBase = kMeetBase + kMeetCounters;
 inline int64_t slot_floats(int columns, int head_dim) { return kSlotHead + int64_t(columns) * head_dim; }
 inline int64_t workspace_floats(int columns, int head_dim) {
     return kSlotBase + 2 * int64_t(kMaxWaves) * slot_floats(columns, head_dim);
