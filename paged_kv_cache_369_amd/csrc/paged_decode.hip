@@ -609,14 +609,49 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV,
     }
 }
 
-// Stretch geometry, identical in every wave: nw waves, wave w owns units
-// [lo(w), lo(w + 1)), lo(w) = floor(w U / nw); every stretch holds at least
-// one unit (nw <= U).
+// Stretch geometry, identical in every wave.  Stretch t of nw covers units
+// [lo(t), lo(t + 1)); every stretch holds at least one unit.  When nw is a
+// multiple of 8, the line is cut into 8 regions, one per XCD (workgroup w runs
+// on XCD w mod 8 and takes stretch (w mod 8) * nw / 8 + w / 8), sized in
+// proportion to the XCD's weight and split evenly among its nw / 8 waves;
+// otherwise the split is even.  One region per XCD keeps the sequences that
+// share a prompt prefix (consecutive in the batch) on one XCD's L2.  On
+// MI355X the odd-numbered XCDs stream 16- and 32-bit tiles about 10 % slower
+// than the even ones (measured per wave; not so for 8-bit tiles), so their
+// regions weigh 14 against 16.
+#ifndef PKV_ODD_XCD_WEIGHT
+#define PKV_ODD_XCD_WEIGHT 14
+#endif
 struct Split {
     uint32_t U, nw;
-    __device__ uint32_t lo(uint32_t w) const { return uint32_t(uint64_t(w) * U / nw); }
-    // the wave whose stretch holds unit u: the largest w with lo(w) <= u
-    __device__ uint32_t wave_of(uint32_t u) const { return uint32_t((uint64_t(u + 1) * nw - 1) / U); }
+    uint32_t m;    // waves per region (0: even split, no regions)
+    uint32_t odd;  // weight of an odd XCD's region (an even one weighs 16)
+    __device__ void init(uint32_t units, uint32_t waves, uint32_t odd_weight) {
+        U = units;
+        nw = waves;
+        odd = odd_weight;
+        m = (waves % 8 == 0 && units >= 2 * waves) ? waves / 8 : 0;
+    }
+    // first unit of region x (weights alternate 16, odd, 16, odd, ...)
+    __device__ uint32_t rb(uint32_t x) const {
+        const uint64_t acc = 16 * ((x + 1) / 2) + uint64_t(odd) * (x / 2);
+        return uint32_t(uint64_t(U) * acc / (64 + 4 * uint64_t(odd)));
+    }
+    __device__ uint32_t lo(uint32_t t) const {
+        if (m == 0) return uint32_t(uint64_t(t) * U / nw);
+        const uint32_t x = t / m, k = t % m;
+        if (x >= 8) return U;
+        const uint32_t r0 = rb(x);
+        return r0 + uint32_t(uint64_t(k) * (rb(x + 1) - r0) / m);
+    }
+    // the stretch that holds unit u: the largest t with lo(t) <= u
+    __device__ uint32_t wave_of(uint32_t u) const {
+        if (m == 0) return uint32_t((uint64_t(u + 1) * nw - 1) / U);
+        uint32_t x = 0;
+        while (x < 7 && u >= rb(x + 1)) ++x;
+        const uint32_t r0 = rb(x);
+        return x * m + uint32_t((uint64_t(u - r0 + 1) * m - 1) / (rb(x + 1) - r0));
+    }
 };
 
 // Combine the partial states of a run cut between waves and write its output.
@@ -866,9 +901,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
     }
-    const Split sp{U, U < nwt ? U : nwt};
+    Split sp;
+    sp.init(U, U < nwt ? U : nwt, KV == kFP8 ? 16u : uint32_t(PKV_ODD_XCD_WEIGHT));
     if (w >= sp.nw) return;
-    const uint32_t lo = sp.lo(w), hi = sp.lo(w + 1);
+    const uint32_t sw = sp.m ? (w % 8) * sp.m + w / 8 : w;  // this wave's stretch
+    const uint32_t lo = sp.lo(sw), hi = sp.lo(sw + 1);
 
     // ---- the sequence holding unit lo: skip whole cached chunks, then walk ----
     Cursor cur;
@@ -1038,7 +1075,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         seen = -1;
         const int f = piece_flags(sl[0]);
         if ((f & kEndsPart) && !(f & kLocal))
-            seen = peek_arrivals(a, unpack_contrib(sl[0].contrib), w);
+            seen = peek_arrivals(a, unpack_contrib(sl[0].contrib), sw);
     };
     peek();
 
@@ -1058,7 +1095,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 holding = false;
                 bool whole = (f & kLocal) != 0;
                 if (!whole &&
-                    merge_across<D>(a, unpack_contrib(sl[0].contrib), w, st, held, cm.hv, seen)) {
+                    merge_across<D>(a, unpack_contrib(sl[0].contrib), sw, st, held, cm.hv, seen)) {
                     lds_get(held, st);
                     whole = true;
                 }
