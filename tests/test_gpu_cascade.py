@@ -18,7 +18,7 @@ from tests import _gpu
 
 pytestmark = pytest.mark.gpu
 
-COUNTERS = (64, 64 + (4 * 4096 + (1 << 18)) * 4)  # byte range of every arrival counter in a workspace
+COUNTERS = (0, (16 + 4 * 4096 + (1 << 18)) * 4)  # byte range of every counter in a workspace (header included)
 
 # groups of (prefix tokens, member lengths): block-aligned and ragged prefixes, members with no private
 # token, a member-less-than-a-chunk group, a group of 19 (ragged last chunk), an unshared sequence
