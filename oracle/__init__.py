@@ -76,6 +76,9 @@ def _load():
                                                p, i32, i32, i32, i32, i32, i32,
                                                f32, f32, f32, i32, i32]
         lib.oracle_paged_attention.restype = ctypes.c_int
+        lib.oracle_paged_attention_varlen.argtypes = [p, p, ctypes.c_int, p, p, p, ctypes.c_int, p, i32,
+                                                      p, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32]
+        lib.oracle_paged_attention_varlen.restype = ctypes.c_int
         lib.oracle_fp8_e4m3_decode_n.argtypes = [p, p, i64]
         lib.oracle_fp8_e4m3_quantise_n.argtypes = [p, p, i64, f32]
         lib.oracle_bf16_to_double_n.argtypes = [p, p, i64]
@@ -174,4 +177,36 @@ def paged_attention(q, q_dtype, k_cache, v_cache, cache_dtype, block_table, cont
                                         ctypes.c_float(v_scale), int(partition_size), int(threads))
     if st != OK:
         raise OracleError(st, "oracle_paged_attention")
+    return out
+
+
+def paged_attention_varlen(q, q_dtype, cu_seqlens_q, k_cache, v_cache, cache_dtype, block_table, context_lens,
+                           scale, k_scale=1.0, v_scale=1.0, block_size=16, threads=0) -> np.ndarray:
+    """float64 [T, H_q, D]: every new query token attends causally to its sequence's context
+    (see ``oracle_paged_attention_varlen``)."""
+    _check(q, q_dtype, "q")
+    _check(k_cache, cache_dtype, "k_cache"); _check(v_cache, cache_dtype, "v_cache")
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    T, Hq, D = q.shape
+    B = context_lens.shape[0]
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if cu.shape != (B + 1,) or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens_q must be [B + 1] and end at the number of query rows")
+    if k_cache.shape != k_pool_shape(NB, Hkv, D, cache_dtype, block_size) or \
+            v_cache.shape != v_pool_shape(NB, Hkv, D, cache_dtype, block_size):
+        raise ValueError("cache shape mismatch")
+    if block_table.ndim != 2 or block_table.shape[0] != B:
+        raise ValueError("table shape mismatch")
+    MB = block_table.shape[1]
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    st = _load().oracle_paged_attention_varlen(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(cu),
+                                               _ptr(k_cache), _ptr(v_cache), DTYPES[cache_dtype],
+                                               _ptr(block_table), MB, _ptr(context_lens),
+                                               B, Hq, Hkv, D, block_size, NB,
+                                               ctypes.c_float(scale), ctypes.c_float(k_scale),
+                                               ctypes.c_float(v_scale), int(threads))
+    if st != OK:
+        raise OracleError(st, "oracle_paged_attention_varlen")
     return out

@@ -9,6 +9,12 @@
  * that decides an fp8 code (the same precision the GPU quantiser uses).
  *
  * Sources (web pages about vLLM / PagedAttention):
+ *  - bytelighting wiki entry "vLLM", paragraph "Flattened 布局与 slot_mapping":
+ *    cu_seqlens (cumulative sequence lengths) keep the requests of a
+ *    flattened batch apart; ai-maas.com page, section 引擎的分层结构 (chunked
+ *    prefill cuts a long prompt into pieces; speculative decoding verifies
+ *    several guessed tokens in one pass): several new query tokens per
+ *    sequence, each attending causally to its context (varlen attention).
  *  - ipipp.com article on vLLM and PagedAttention (2026-09-14),
  *    section 二 "PagedAttention分页原理深度剖析": the KV cache is cut into
  *    fixed blocks of 16 tokens; a block table maps each logical block of a
@@ -333,6 +339,17 @@ static double kv_at(const attn_job* J, int is_v, int s, int g, int t, int d)
     return J->cache_dtype == ORC_FP8_E4M3 ? x * (is_v ? J->v_scale : J->k_scale) : x;
 }
 
+/* Score of query row qr (its head h) against logical token t of sequence s:
+ * scale * q[qr][h] . k_t.  In decode, query row qr is sequence s itself. */
+static double score_row(const attn_job* J, int s, int64_t qr, int h, int g, int t)
+{
+    double acc = 0.0;
+    size_t qbase = ((size_t)qr * J->num_heads + h) * (size_t)J->head_dim;
+    for (int d = 0; d < J->head_dim; ++d)
+        acc += load_as_double(J->q, J->q_dtype, qbase + d) * kv_at(J, 0, s, g, t, d);
+    return J->scale * acc;
+}
+
 /* Score of query (s, h) against logical token t: scale * q . k_t */
 static double score_at(const attn_job* J, int s, int h, int g, int t)
 {
@@ -448,6 +465,162 @@ static void* attn_worker(void* arg)
         }
     }
     return NULL;
+}
+
+/*
+ * Several new query tokens per sequence (chunked prefill, speculative
+ * verification).  Query row qr belongs to sequence s with cu[s] <= qr <
+ * cu[s+1]; it is the i-th of the sequence's n = cu[s+1] - cu[s] new tokens,
+ * which are the last n of its L cached tokens, so it sits at position
+ * p = L - n + i and attends causally to tokens [0, p]:
+ *   m = max_{t<=p} score_t,  out = sum_{t<=p} exp(score_t - m) v_t / sum_{t<=p} exp(score_t - m)
+ */
+static void attend_causal(const attn_job* J, int s, int64_t qr, int h, int limit, double* row)
+{
+    int G = J->num_heads / J->num_kv_heads;
+    int g = h / G;
+    double* w;
+    double m = -INFINITY, Z = 0.0;
+    for (int d = 0; d < J->head_dim; ++d)
+        row[d] = 0.0;
+    if (limit <= 0)
+        return;
+    w = (double*)malloc(sizeof(double) * (size_t)limit);
+    for (int t = 0; t < limit; ++t) {
+        w[t] = score_row(J, s, qr, h, g, t);
+        if (w[t] > m)
+            m = w[t];
+    }
+    for (int t = 0; t < limit; ++t) {
+        w[t] = exp(w[t] - m);
+        Z += w[t];
+    }
+    for (int t = 0; t < limit; ++t) {
+        double pr = w[t] / Z;
+        for (int d = 0; d < J->head_dim; ++d)
+            row[d] += pr * kv_at(J, 1, s, g, t, d);
+    }
+    free(w);
+}
+
+int oracle_num_threads(int requested);
+
+typedef struct {
+    attn_job* J;
+    const int32_t* cu;       /* [num_seqs + 1] */
+    const int32_t* row_seq;  /* [num_rows] sequence of each query row */
+    int64_t num_rows;
+} varlen_job;
+
+static void* varlen_worker(void* arg)
+{
+    varlen_job* V = (varlen_job*)arg;
+    attn_job* J = V->J;
+    int64_t total = V->num_rows * J->num_heads;
+    for (;;) {
+        int64_t item;
+        pthread_mutex_lock(&J->lock);
+        item = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (item >= total)
+            break;
+        {
+            int64_t qr = item / J->num_heads;
+            int h = (int)(item % J->num_heads);
+            int s = V->row_seq[qr];
+            int n = V->cu[s + 1] - V->cu[s];
+            int i = (int)(qr - V->cu[s]);
+            int pos = J->context_lens[s] - n + i;
+            attend_causal(J, s, qr, h, pos + 1, J->out + (size_t)item * J->head_dim);
+        }
+    }
+    return NULL;
+}
+
+/*
+ * out[qr][h][:] (double) for every query row qr in [0, cu_seqlens_q[num_seqs])
+ * as described at attend_causal.  Errors: as oracle_paged_attention, plus
+ * cu_seqlens_q not starting at 0 or decreasing, or a sequence with more new
+ * tokens than cached tokens.
+ */
+int oracle_paged_attention_varlen(double* out, const void* q, int q_dtype, const int32_t* cu_seqlens_q,
+                                  const void* k_cache, const void* v_cache, int cache_dtype,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                  int32_t num_threads)
+{
+    attn_job J;
+    varlen_job V;
+    int32_t* row_seq;
+    int64_t rows;
+    int nt;
+    pthread_t* th;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0
+        || num_blocks < 0 || max_blocks_per_seq < 0)
+        return ORC_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0)
+        return ORC_ERR_INVALID_ARG;
+    if (!(q_dtype == ORC_F32 || q_dtype == ORC_BF16) || elt_size(cache_dtype) == 0)
+        return ORC_ERR_UNSUPPORTED;
+    if (head_dim % k_chunk_elems(cache_dtype) != 0)
+        return ORC_ERR_UNSUPPORTED;
+    if (cu_seqlens_q[0] != 0)
+        return ORC_ERR_INVALID_ARG;
+    for (int s = 0; s < num_seqs; ++s) {
+        int64_t L = context_lens[s];
+        int64_t n = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+        int64_t nb = (L + block_size - 1) / block_size;
+        if (n < 0 || n > L || L > (int64_t)max_blocks_per_seq * block_size)
+            return ORC_ERR_INVALID_ARG;
+        for (int64_t j = 0; j < nb; ++j) {
+            int32_t b = block_table[(size_t)s * max_blocks_per_seq + j];
+            if (b < 0 || b >= num_blocks)
+                return ORC_ERR_INVALID_ARG;
+        }
+    }
+    rows = num_seqs > 0 ? cu_seqlens_q[num_seqs] : 0;
+    row_seq = (int32_t*)malloc(sizeof(int32_t) * (size_t)(rows > 0 ? rows : 1));
+    for (int s = 0; s < num_seqs; ++s)
+        for (int32_t r = cu_seqlens_q[s]; r < cu_seqlens_q[s + 1]; ++r)
+            row_seq[r] = s;
+
+    J.out = out;
+    J.q = q;
+    J.q_dtype = q_dtype;
+    J.k_cache = k_cache;
+    J.v_cache = v_cache;
+    J.cache_dtype = cache_dtype;
+    J.block_table = block_table;
+    J.max_blocks_per_seq = max_blocks_per_seq;
+    J.context_lens = context_lens;
+    J.num_seqs = num_seqs;
+    J.num_heads = num_heads;
+    J.num_kv_heads = num_kv_heads;
+    J.head_dim = head_dim;
+    J.block_size = block_size;
+    J.scale = (double)scale;
+    J.k_scale = (double)k_scale;
+    J.v_scale = (double)v_scale;
+    J.partition_size = 0;
+    J.next = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    V.J = &J;
+    V.cu = cu_seqlens_q;
+    V.row_seq = row_seq;
+    V.num_rows = rows;
+
+    nt = oracle_num_threads(num_threads);
+    th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    for (int i = 0; i < nt; ++i)
+        pthread_create(&th[i], NULL, varlen_worker, &V);
+    for (int i = 0; i < nt; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    free(row_seq);
+    pthread_mutex_destroy(&J.lock);
+    return ORC_OK;
 }
 
 /* Number of worker threads actually used for a given request (0 = all cores). */
