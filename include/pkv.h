@@ -75,8 +75,8 @@ typedef enum pkv_status {
  * chunked-K / dimension-major-V pool layout and the workspace query that
  * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
  * use and is left that way by every call; 4 = the block manager and
- * paged_kv_copy_blocks; 5 = paged_attention_decode_cascade and
- * pkv_bm_shared_prefix). */
+ * paged_kv_copy_blocks; 5 = paged_attention_decode_cascade; 6 =
+ * paged_attention_varlen). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -244,6 +244,62 @@ int paged_attention_decode_cascade(void* out,
                                    int32_t partition_size,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * paged_attention_varlen_workspace_bytes -- workspace size for
+ * paged_attention_varlen: the decode workspace with merge slots 16 columns
+ * wide.  Independent of the number of query rows.  Returns 0 for arguments
+ * paged_attention_decode would reject.
+ */
+size_t paged_attention_varlen_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t partition_size);
+
+/*
+ * paged_attention_varlen -- several new query tokens per sequence over the
+ * paged cache (chunked prefill, verification of speculated tokens):
+ *   out[r][h][:] = sum_{t <= p} softmax_t(scale * q[r][h] . k_t) v_t
+ * for every query row r of sequence s (cu_seqlens_q[s] <= r <
+ * cu_seqlens_q[s+1]), the i-th of its n = cu_seqlens_q[s+1] -
+ * cu_seqlens_q[s] new tokens, which are the last n of its L_s cached tokens:
+ * p = L_s - n + i (causal: a token sees its context and the new tokens up to
+ * itself).  The new tokens' K/V must already be in the cache
+ * (paged_kv_write takes any number of tokens per sequence).
+ *   Source: bytelighting wiki "vLLM", "Flattened 布局与 slot_mapping"
+ *   (cu_seqlens keeps the requests of a flattened batch apart); ai-maas.com
+ *   article, 引擎的分层结构 (chunked prefill; speculative decoding verifies
+ *   several guessed tokens in one pass).
+ *
+ * All arguments as in paged_attention_decode, except:
+ * q, out         [num_q_rows][num_heads][head_dim] in q_dtype: rows are the
+ *                new tokens of all sequences, sequence by sequence.
+ * cu_seqlens_q   [num_seqs + 1] int32 device array: sequence s owns rows
+ *                [cu_seqlens_q[s], cu_seqlens_q[s+1]); nondecreasing from 0
+ *                to num_q_rows.  A sequence's count is clamped into
+ *                [0, L_s]; rows a sequence does not claim, or that fall
+ *                outside [0, num_q_rows), are not written (memory-safe for
+ *                any contents).
+ * The kernel serves 16 / (query heads per run) consecutive new tokens of a
+ * sequence times the run's heads in one matrix tile (4 tokens for a GQA
+ * group of 4), so each such group of tokens reads the context once, up to
+ * the group's last token.
+ * workspace      >= paged_attention_varlen_workspace_bytes(...) bytes, same
+ *                zero-fill and reuse contract as paged_attention_decode.
+ * Errors: as paged_attention_decode (PKV_ERR_UNSUPPORTED also when the units
+ * or num_q_rows * num_heads * head_dim reach 2^31); PKV_ERR_INVALID_ARG for a
+ * NULL cu_seqlens_q or num_q_rows < 0.  num_q_rows == 0 is a no-op.
+ */
+int paged_attention_varlen(void* out,
+                           const void* q, int q_dtype, const int32_t* cu_seqlens_q, int32_t num_q_rows,
+                           const void* k_cache, const void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * pkv_check_inputs -- count the contents of the index arrays that the kernels

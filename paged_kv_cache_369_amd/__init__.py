@@ -68,6 +68,11 @@ def _load():
     lib.paged_attention_decode_cascade.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p, p, p,
                                                    i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
     lib.paged_attention_decode_cascade.restype = ctypes.c_int
+    lib.paged_attention_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_varlen_workspace_bytes.restype = sz
+    lib.paged_attention_varlen.argtypes = [p, p, ctypes.c_int, p, i32, p, p, ctypes.c_int, p, i32, p,
+                                           i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
+    lib.paged_attention_varlen.restype = ctypes.c_int
     lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
     lib.pkv_check_inputs.restype = ctypes.c_int
     i64 = ctypes.c_int64
@@ -260,6 +265,40 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_table, contex
                                             float(scale), float(k_scale), float(v_scale), int(partition_size),
                                             ws_ptr, ws_bytes, _stream(stream))
     _check(st, "paged_attention_decode_cascade")
+
+
+def paged_attention_varlen_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                           max_blocks_per_seq: int, block_size: int = BLOCK_SIZE,
+                                           partition_size: int = 0) -> int:
+    return int(_load().paged_attention_varlen_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                              max_blocks_per_seq, block_size, partition_size))
+
+
+def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, context_lens, scale: float,
+                           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0, workspace=None,
+                           stream=None) -> None:
+    """Several new query tokens per sequence: q and out are [T, H, D] (rows grouped by sequence through
+    cu_seqlens_q [B + 1]); row i of sequence s attends causally to its first L_s - n_s + i + 1 cached tokens."""
+    lib = _load()
+    T, Hq, D = q.shape
+    NB, Hkv, Dc = _pools(k_cache, v_cache)
+    if out.shape != q.shape or Dc != D:
+        raise ValueError("shape mismatch")
+    B = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.shape != (B + 1,):
+        raise ValueError("block_table must be [B, max_blocks] and cu_seqlens_q [B + 1]")
+    MB = block_table.shape[1]
+    need = paged_attention_varlen_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
+    if workspace is None and need > 0:
+        workspace = _default_workspace(q.device, need)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attention_varlen(_dev(out, "out"), _dev(q, "q"), _dtype_code(q), _dev(cu_seqlens_q, "cu_seqlens_q"),
+                                    T, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+                                    _dev(block_table, "block_table"), MB, _dev(context_lens, "context_lens"),
+                                    B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), float(k_scale), float(v_scale),
+                                    int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "paged_attention_varlen")
 
 
 def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_mapping=None, stream=None):

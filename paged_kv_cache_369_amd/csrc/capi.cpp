@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -97,7 +97,8 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 float scale, float k_scale, float v_scale, int32_t partition_size, const int32_t* prefix_leader,
-                const int32_t* prefix_blocks, bool cascade, void* workspace, size_t workspace_bytes, void* stream) {
+                const int32_t* prefix_blocks, bool cascade, const int32_t* cu_q, int32_t num_q_rows, bool multi,
+                void* workspace, size_t workspace_bytes, void* stream) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         num_blocks < 0 || max_blocks_per_seq < 0)
         return PKV_ERR_INVALID_ARG;
@@ -117,9 +118,12 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
     if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
     const int rh = pkv::run_heads(num_heads / num_kv_heads);
     const int runs = num_heads / rh;
-    // units (sequence, run, block) are counted in 32 bits; a prefix run adds at most one sequence's worth
-    if (int64_t(num_seqs) * runs * max_blocks_per_seq * (cascade ? 2 : 1) >= (int64_t(1) << 31))
-        return PKV_ERR_UNSUPPORTED;
+    // units (sequence, run, block) are counted in 32 bits; a prefix run adds at most one sequence's worth,
+    // and with several queries every token group of a sequence reads at most its whole table row
+    const int64_t groups = multi ? int64_t(num_q_rows) / prefix_members(rh) + num_seqs : num_seqs;
+    if (multi && num_q_rows < 0) return PKV_ERR_INVALID_ARG;
+    if (groups * runs * max_blocks_per_seq * (cascade ? 2 : 1) >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+    if (multi && int64_t(num_q_rows) * num_heads * head_dim >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
     const int64_t state_bytes = int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim) * 4;
     if (cascade && (state_bytes >= (int64_t(1) << 31) || int64_t(num_seqs) * runs > pkv::kMeetCounters))
         return PKV_ERR_UNSUPPORTED;
@@ -127,15 +131,20 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
     if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
         return PKV_ERR_INVALID_ARG;
     if (cascade && (!prefix_leader || !prefix_blocks)) return PKV_ERR_INVALID_ARG;
+    if (multi && !cu_q) return PKV_ERR_INVALID_ARG;
+    if (multi && num_q_rows == 0) return PKV_OK;
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(workspace, 16) ||
-        !aligned(prefix_leader, 4) || !aligned(prefix_blocks, 4))
+        !aligned(prefix_leader, 4) || !aligned(prefix_blocks, 4) || !aligned(cu_q, 4))
         return PKV_ERR_ALIGNMENT;
 
-    const size_t need = cascade ? paged_attention_cascade_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                                          max_blocks_per_seq, block_size, partition_size)
-                                : paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                                  max_blocks_per_seq, block_size, partition_size);
+    const size_t need =
+        cascade ? paged_attention_cascade_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                          max_blocks_per_seq, block_size, partition_size)
+        : multi ? paged_attention_varlen_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                         max_blocks_per_seq, block_size, partition_size)
+                : paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                  block_size, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
     pkv::DecodeArgs a{};
@@ -170,6 +179,13 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
         a.pstate = a.ws + base;
         a.sstate = a.pstate + pkv::align_floats(int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim));
         a.state_bytes = int32_t(state_bytes);
+    } else if (multi) {
+        // a run's columns hold `members` new tokens of one sequence times rh heads
+        const int members = prefix_members(rh);
+        a.slot_floats = int32_t(pkv::slot_floats(members * rh, head_dim));
+        a.members = members;
+        a.cu_q = cu_q;
+        a.num_q_rows = num_q_rows;
     } else {
         a.slot_floats = int32_t(pkv::slot_floats(rh, head_dim));
     }
@@ -194,7 +210,8 @@ int paged_attention_decode(void* out,
                            void* stream) {
     return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
-                       partition_size, nullptr, nullptr, false, workspace, workspace_bytes, stream);
+                       partition_size, nullptr, nullptr, false, nullptr, 0, false, workspace, workspace_bytes,
+                       stream);
 }
 
 size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -223,7 +240,35 @@ int paged_attention_decode_cascade(void* out,
                                    void* stream) {
     return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
-                       partition_size, prefix_leader, prefix_blocks, true, workspace, workspace_bytes, stream);
+                       partition_size, prefix_leader, prefix_blocks, true, nullptr, 0, false, workspace,
+                       workspace_bytes, stream);
+}
+
+size_t paged_attention_varlen_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t partition_size) {
+    if (paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                                        partition_size) == 0)
+        return 0;
+    const int rh = pkv::run_heads(num_heads / num_kv_heads);
+    return size_t(pkv::workspace_floats(prefix_members(rh) * rh, head_dim)) * sizeof(float);
+}
+
+int paged_attention_varlen(void* out,
+                           const void* q, int q_dtype, const int32_t* cu_seqlens_q, int32_t num_q_rows,
+                           const void* k_cache, const void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
+                       partition_size, nullptr, nullptr, false, cu_seqlens_q, num_q_rows, true, workspace,
+                       workspace_bytes, stream);
 }
 
 int paged_kv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_kv_heads, int32_t head_dim,

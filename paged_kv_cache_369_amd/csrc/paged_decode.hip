@@ -327,7 +327,16 @@ struct SeqInfo {
     int len;  // clamped context length (0 past the batch)
     int pbe;  // blocks read by a prefix run (0: plain)
     int cl;   // sequence whose prefix runs cover s (-1: plain)
+    int nq;   // several queries: new query tokens, clamped into [0, len]
+    int q0;   // several queries: first query row
 };
+
+// Several queries: blocks the run of token group g needs (through its last
+// token, at position len - nq + min((g + 1) tpr, nq)).
+__device__ __forceinline__ int group_blocks(int len, int nq, int tpr, int g) {
+    const int last = min((g + 1) * tpr, nq);
+    return (len - nq + last + kBlockTokens - 1) / kBlockTokens;
+}
 
 __device__ __forceinline__ int shared_blocks(const DecodeArgs& a, int s, int L) {
     const int pb = a.prefix_blocks[s];
@@ -335,12 +344,17 @@ __device__ __forceinline__ int shared_blocks(const DecodeArgs& a, int s, int L) 
     return pb < 0 ? 0 : (pb > full ? full : pb);
 }
 
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ SeqInfo seq_info(const DecodeArgs& a, int s) {
-    SeqInfo r{0, 0, -1};
+    SeqInfo r{0, 0, -1, 0, 0};
     if (s >= a.num_seqs) return r;
     r.len = clamped_len(a, s);
-    if constexpr (CAS) {
+    if constexpr (M == kModeMulti) {
+        r.q0 = a.cu_q[s];
+        const int n = a.cu_q[s + 1] - r.q0;
+        r.nq = n < 0 ? 0 : (n > r.len ? r.len : n);
+    }
+    if constexpr (M == kModeShared) {
         const int pbs = shared_blocks(a, s, r.len);
         const int ld = a.prefix_leader[s];
         if (pbs > 0 && ld >= 0 && ld <= s) {
@@ -355,8 +369,15 @@ __device__ __forceinline__ SeqInfo seq_info(const DecodeArgs& a, int s) {
     return r;
 }
 
-// Units of sequence s: its suffix (or plain) runs, plus the prefix runs it leads.
+// Units of sequence s: its suffix (or plain) runs, plus the prefix runs it
+// leads; with several queries, the runs of every token group.
+template <int M>
 __device__ __forceinline__ uint32_t seq_units(const DecodeArgs& a, const SeqInfo& si, int s) {
+    if constexpr (M == kModeMulti) {
+        uint32_t b = 0;
+        for (int g = 0; g * a.members < si.nq; ++g) b += uint32_t(group_blocks(si.len, si.nq, a.members, g));
+        return b * uint32_t(a.runs);
+    }
     const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
     return uint32_t(nb - si.pbe + (si.cl == s ? si.pbe : 0)) * uint32_t(a.runs);
 }
@@ -371,35 +392,35 @@ struct Cursor {
     uint32_t tot;    // units in the chunk
 };
 
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int base) {
     const int s = base + lane_id();
     c.base = base;
-    c.si = seq_info<CAS>(a, s);
-    c.inc = wave_scan(seq_units(a, c.si, s));
+    c.si = seq_info<M>(a, s);
+    c.inc = wave_scan(seq_units<M>(a, c.si, s));
     c.tot = __builtin_amdgcn_readlane(c.inc, 63);
 }
 
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ void cursor_advance(Cursor& c, const DecodeArgs& a) {
     c.start += c.tot;
-    cursor_load<CAS>(c, a, c.base + 64);
+    cursor_load<M>(c, a, c.base + 64);
 }
 
 // Lane of the chunk holding the sequence that contains unit u (u < U).
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ int cursor_find(Cursor& c, const DecodeArgs& a, uint32_t u) {
-    while (c.start + c.tot <= u) cursor_advance<CAS>(c, a);
+    while (c.start + c.tot <= u) cursor_advance<M>(c, a);
     return __builtin_ctzll(__ballot(c.start + c.inc > u));
 }
 
 // Lane of the next sequence with units after lane i (one exists).
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ int cursor_next(Cursor& c, const DecodeArgs& a, int i) {
-    if constexpr (!CAS) {  // a sequence has units exactly when it has tokens
+    if constexpr (M == kModePlain) {  // a sequence has units exactly when it has tokens
         unsigned long long m = __ballot(lane_id() > i && c.si.len > 0);
         while (m == 0) {
-            cursor_advance<CAS>(c, a);
+            cursor_advance<M>(c, a);
             m = __ballot(c.si.len > 0);
         }
         return __builtin_ctzll(m);
@@ -407,7 +428,7 @@ __device__ __forceinline__ int cursor_next(Cursor& c, const DecodeArgs& a, int i
     const uint32_t prev = __shfl_up(c.inc, 1);
     unsigned long long m = __ballot(lane_id() > i && c.inc != (lane_id() == 0 ? 0u : prev));
     while (m == 0) {
-        cursor_advance<CAS>(c, a);
+        cursor_advance<M>(c, a);
         const uint32_t p = __shfl_up(c.inc, 1);
         m = __ballot(c.inc != (lane_id() == 0 ? 0u : p));
     }
@@ -430,14 +451,14 @@ __device__ __forceinline__ Cols plain_cols(const DecodeArgs& a, int s, int hg) {
 
 // Columns of prefix run (s, hg): column col serves head hg * rh + col % rh of
 // sequence s + col / rh, if that sequence is covered by s's prefix runs.
-template <bool CAS>
+template <int M>
 __device__ __forceinline__ Cols prefix_cols(const DecodeArgs& a, const Cursor& cur, int i, int s, int hg, int pbe) {
     const int col = lane_id() & 15;
     const int member = col / a.rh;
     const int sm = s + member;
     const int src = min(i + member, 63);
-    SeqInfo x{__shfl(cur.si.len, src), 0, __shfl(cur.si.cl, src)};
-    if (i + member >= 64) x = seq_info<CAS>(a, sm);  // in the next chunk of the cursor
+    SeqInfo x{__shfl(cur.si.len, src), 0, __shfl(cur.si.cl, src), 0, 0};
+    if (i + member >= 64) x = seq_info<M>(a, sm);  // in the next chunk of the cursor
     const bool hv = col < a.members * a.rh && x.cl == s;
     const bool sne = (x.len + kBlockTokens - 1) / kBlockTokens > pbe;
     return Cols{int64_t(hv ? sm : s) * a.num_heads + hg * a.rh + col % a.rh, hv, sne};
@@ -523,9 +544,11 @@ __device__ __forceinline__ void run_close(const Run<NVC>& r, State<NVC>& st) {
     for (int c = 0; c < NVC; ++c) st.acc[c] = r.acc[c];
 }
 
-// Steps 2-4 for one block with nv valid tokens.
-template <int KV, int D>
-__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv,
+// Steps 2-4 for one block with nv valid tokens.  With CAUSAL, this lane's
+// column scores only the block's first `upto` tokens (its token's position is
+// upto - 1 relative to the block); the values stay masked by nv only.
+template <int KV, int D, bool CAUSAL>
+__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv, int upto,
                                              const QOp<KV> (&qop)[Geo<KV, D>::NQ], Run<Geo<KV, D>::NVC>& rs) {
     using GE = Geo<KV, D>;
     const int g = lane_id() >> 4;
@@ -552,9 +575,10 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV,
     }
     // 3. online softmax for head `col`
     const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
+    const int scnt = CAUSAL ? min(cnt, max(upto - 4 * g, 0)) : cnt;  // ... that this column may see
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = r < cnt ? sacc[r] * a.score_scale : kNegInf;
+    for (int r = 0; r < 4; ++r) sv[r] = r < scnt ? sacc[r] * a.score_scale : kNegInf;
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -828,6 +852,8 @@ struct Piece {
     uint32_t contrib; // a cut run's waves: w0 | (w1 << 13) | first_in_slot1 << 26
     uint32_t cols;    // bit c: column c holds a head; bit 16 + c: its sequence has suffix runs (prefix runs)
     int ids;          // lane l < p1 - p0: physical block of the piece's l-th block
+    int qrow0;        // several queries: query row of column 0's token
+    int cpos0;        // several queries: column 0's token position + 1 - context length (<= 0)
 };
 
 static_assert(kMaxWaves <= (1 << 13), "wave indices are packed in 13 bits");
@@ -852,6 +878,8 @@ __device__ __forceinline__ Cols piece_cols(const DecodeArgs& a, const Piece& p) 
     const int hg = piece_hg(p);
     if (piece_kind(p) == 1)
         return Cols{int64_t(p.s + (hv ? col / a.rh : 0)) * a.num_heads + hg * a.rh + col % a.rh, hv, sne};
+    if (piece_kind(p) == 3)  // several queries: column col is token col / rh of the group, head col % rh
+        return Cols{int64_t(hv ? p.qrow0 + col / a.rh : 0) * a.num_heads + hg * a.rh + col % a.rh, hv, false};
     return Cols{int64_t(p.s) * a.num_heads + hg * a.rh + (hv ? col : 0), hv, sne};
 }
 
@@ -866,7 +894,7 @@ template <int KV, int D>
 constexpr int kWavesPerSimd = (KV == kF32 && D == 128) ? 1 : 2;
 #endif
 
-template <int KV, int D, int P, bool CAS>
+template <int KV, int D, int P, int M>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D>))) void paged_decode_kernel(
     DecodeArgs a) {
     using GE = Geo<KV, D>;
@@ -885,15 +913,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     for (int base = 0; base < a.num_seqs; base += 64 * kLenChunks) {
         SeqInfo si[kLenChunks];
 #pragma unroll
-        for (int c = 0; c < kLenChunks; ++c) si[c] = seq_info<CAS>(a, base + 64 * c + lane);
+        for (int c = 0; c < kLenChunks; ++c) si[c] = seq_info<M>(a, base + 64 * c + lane);
 #pragma unroll
         for (int c = 0; c < kLenChunks; ++c) {
             const int cb = base + 64 * c;
             if (cb >= a.num_seqs) break;
-            const uint32_t t = __builtin_amdgcn_readlane(wave_scan(seq_units(a, si[c], cb + lane)), 63);
+            const uint32_t t = __builtin_amdgcn_readlane(wave_scan(seq_units<M>(a, si[c], cb + lane)), 63);
             if (base == 0) ctot[c] = t;
             U += t;
-            unsigned long long empty = __ballot(cb + lane < a.num_seqs && si[c].len == 0);
+            unsigned long long empty = __ballot(M != kModeMulti && cb + lane < a.num_seqs && si[c].len == 0);
             while (empty) {
                 const int se = cb + __builtin_ctzll(empty);
                 empty &= empty - 1;
@@ -922,18 +950,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
     }
-    cursor_load<CAS>(cur, a, 64 * chunk);
+    cursor_load<M>(cur, a, 64 * chunk);
     int i = 0;
     // Runs of a sequence: npre prefix runs over blocks [0, pbe) (when it leads
     // a prefix group), then its runs over blocks [pbe, nb).
-    int L = 0, nb = 0, pbe = 0, npre = 0;
+    // With several queries, a sequence's runs are its token groups (of
+    // a.members new tokens) times its head groups, run r being group r / runs.
+    int L = 0, nb = 0, pbe = 0, npre = 0, nq = 0, q0 = 0;
     auto enter = [&]() {
         L = __builtin_amdgcn_readlane(cur.si.len, i);
         nb = (L + kBlockTokens - 1) / kBlockTokens;
-        if constexpr (CAS) {
+        if constexpr (M == kModeShared) {
             pbe = __builtin_amdgcn_readlane(cur.si.pbe, i);
             npre = __builtin_amdgcn_readlane(cur.si.cl, i) == cur.base + i ? a.runs : 0;
         }
+        if constexpr (M == kModeMulti) {
+            nq = __builtin_amdgcn_readlane(cur.si.nq, i);
+            q0 = __builtin_amdgcn_readlane(cur.si.q0, i);
+        }
+    };
+    auto nruns = [&]() -> int {
+        if constexpr (M == kModeMulti) return (nq + a.members - 1) / a.members * a.runs;
+        return npre + (nb > pbe ? a.runs : 0);
     };
     int r = 0, j = 0;
     uint32_t run_first = 0;
@@ -942,13 +980,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     bool fresh = true;   // the next piece starts a new softmax state
     // position the walker at unit `at` (the start of the stretch)
     auto seek = [&](uint32_t at) {
-        i = cursor_find<CAS>(cur, a, at);
+        i = cursor_find<M>(cur, a, at);
         enter();
-        const uint32_t units = uint32_t(npre * pbe + (nb - pbe) * a.runs);
-        const uint32_t seq_first = cur.start + __builtin_amdgcn_readlane(cur.inc, i) - units;
-        uint32_t o = at - seq_first;
+        const uint32_t prev = i > 0 ? uint32_t(__builtin_amdgcn_readlane(cur.inc, i - 1)) : 0u;
+        uint32_t o = at - (cur.start + prev);
         const uint32_t pre_units = uint32_t(npre * pbe);
-        if (o < pre_units) {
+        if constexpr (M == kModeMulti) {
+            int g = 0;
+            while (true) {
+                const uint32_t gb = uint32_t(group_blocks(L, nq, a.members, g));
+                if (o < gb * uint32_t(a.runs)) {
+                    r = g * a.runs + int(o / gb);
+                    j = int(o % gb);
+                    break;
+                }
+                o -= gb * uint32_t(a.runs);
+                ++g;
+            }
+            run_first = at - uint32_t(j);
+        } else if (o < pre_units) {
             r = int(o / uint32_t(pbe));
             j = int(o % uint32_t(pbe));
             run_first = at - uint32_t(j);
@@ -981,8 +1031,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
         const int s = cur.base + i;
         const bool pre = r < npre;
-        const int hg = pre ? r : r - npre;
-        const uint32_t run_end = run_first + uint32_t(pre ? pbe : nb - pbe);
+        const int grp = M == kModeMulti ? r / a.runs : 0;  // several queries: the token group
+        const int hg = M == kModeMulti ? r % a.runs : (pre ? r : r - npre);
+        const int rlen = M == kModeMulti ? group_blocks(L, nq, a.members, grp) : (pre ? pbe : nb - pbe);
+        const uint32_t run_end = run_first + uint32_t(rlen);
         const uint32_t seg_end = run_end < cut ? run_end : cut;
         const uint32_t pe = seg_end < u + 64u ? seg_end : u + 64u;
         const bool close = pe == seg_end;
@@ -996,12 +1048,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         pc.p1 = spos + (pe - u);
         pc.s = s;
         pc.lim0 = (pre ? pbe * kBlockTokens : L) - j * kBlockTokens;
-        pc.info = hg | ((pre ? 1 : (pbe > 0 ? 2 : 0)) << 16) | (f << 20);
+        pc.info = hg | ((M == kModeMulti ? 3 : (pre ? 1 : (pbe > 0 ? 2 : 0))) << 16) | (f << 20);
         pc.contrib = (f & kEndsPart) && !(f & kLocal) ? pack_contrib(contributors(sp, run_first, run_end - 1)) : 0u;
         pc.cols = (1u << a.rh) - 1u;
-        if constexpr (CAS) {
+        if constexpr (M == kModeMulti) {
+            // columns: a.members tokens of the group (those that exist) times rh heads
+            const int first = grp * a.members;
+            const int ntok = min(a.members, nq - first);
+            const bool rows_ok = q0 >= 0 && int64_t(q0) + first + ntok <= int64_t(a.num_q_rows);
+            pc.cols = rows_ok ? (ntok * a.rh >= 32 ? 0xffffffffu : (1u << (ntok * a.rh)) - 1u) & 0xffffu : 0u;
+            pc.qrow0 = q0 + first;
+            pc.cpos0 = first + 1 - nq;
+        }
+        if constexpr (M == kModeShared) {
             if (pre) {
-                const Cols x = prefix_cols<CAS>(a, cur, i, s, hg, pbe);
+                const Cols x = prefix_cols<M>(a, cur, i, s, hg, pbe);
                 const uint32_t hvm = uint32_t(__ballot(x.hv)) & 0xffffu;  // row group 0 holds every column
                 const uint32_t snem = uint32_t(__ballot(x.hv && x.sne)) & 0xffffu;
                 pc.cols = hvm | (snem << 16);
@@ -1019,8 +1080,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
         if (close && seg_end == run_end && u < hi) {  // the next run
             run_first = run_end;
-            if (++r == npre + (nb > pbe ? a.runs : 0)) {
-                i = cursor_next<CAS>(cur, a, i);
+            if (++r == nruns()) {
+                i = cursor_next<M>(cur, a, i);
                 enter();
                 r = 0;
             }
@@ -1047,10 +1108,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     }
     Run<NVC> rs;
     run_reset(rs);
+    // several queries: this lane's column token position + 1 - context length;
+    // a tile with `lim` tokens left of the context shows it lim + crel of them
+    int crel = 0;
+    auto set_crel = [&]() {
+        if constexpr (M == kModeMulti) crel = sl[0].cpos0 + (lane & 15) / a.rh;
+    };
+    set_crel();
 
     // the tile at stream position pos: its piece's block id and valid tokens
     // (a position past the stream loads block 0 of KV head 0 and counts no tokens)
-    auto issue = [&](T& tb, int& nv, uint32_t pos) {
+    auto issue = [&](T& tb, int& nv, int& lraw, uint32_t pos) {
         int id = 0, kvh = 0, lim = 0;
         bool real = false;
 #pragma unroll
@@ -1065,6 +1133,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
         const bool ok = real && id >= 0 && id < a.num_blocks;
         nv = ok ? min(kBlockTokens, lim) : 0;
+        lraw = lim;
         load_tile<KV, D>(a, ok ? kvh : 0, ok ? id : 0, tb);
     };
 
@@ -1100,7 +1169,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                     whole = true;
                 }
                 if (whole) {
-                    if constexpr (CAS) {
+                    if constexpr (M == kModeShared) {
                         if (piece_kind(sl[0]) == 1)
                             meet_prefix<QT, D>(a, sl[0].s, piece_hg(sl[0]), cm, st);
                         else if (piece_kind(sl[0]) == 2)
@@ -1125,14 +1194,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             const Cols c1 = piece_cols(a, sl[1]);
             load_q<KV, D>(a, c1.row, c1.hv, qn);
         }
+        set_crel();
         peek();
     };
 
     // ---- the tile stream: consume position t while position t + P - 1 loads ----
     T buf[P];
     int nvb[P];  // valid tokens of the buffered block (0: the block contributes nothing)
+    int lrb[P];  // tokens of the context at and after the buffered block's first token
 #pragma unroll
-    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], uint32_t(k));
+    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], lrb[k], uint32_t(k));
     bool more = true;
     for (uint32_t t = 0; more; t += P) {
 #pragma unroll
@@ -1140,8 +1211,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             const uint32_t tp = t + uint32_t(k);
             more = more && tp < sl[0].p1;
             if (more) {
-                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], tp + uint32_t(P - 1));
-                consume_tile<KV, D>(a, buf[k], nvb[k], qop, rs);
+                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], lrb[(k + P - 1) % P], tp + uint32_t(P - 1));
+                consume_tile<KV, D, M == kModeMulti>(a, buf[k], nvb[k], lrb[k] + crel, qop, rs);
                 if (tp + 1 == sl[0].p1) next_piece();
             }
         }
@@ -1173,10 +1244,10 @@ int device_cus() {
     return cached;
 }
 
-template <int KV, int D, bool CAS>
+template <int KV, int D, int M>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int P = Depth<KV, D>::P;
-    auto kern = paged_decode_kernel<KV, D, P, CAS>;
+    auto kern = paged_decode_kernel<KV, D, P, M>;
     static int waves_per_cu = 0;  // occupancy of this instance (64-thread workgroups)
     if (waves_per_cu == 0) {
         int n = 0;
@@ -1194,21 +1265,22 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-template <bool CAS>
+template <int M>
 hipError_t launch_c(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
-    if (cache_dtype == kF32 && head_dim == 64) return launch_t<kF32, 64, CAS>(a, stream);
-    if (cache_dtype == kF32 && head_dim == 128) return launch_t<kF32, 128, CAS>(a, stream);
-    if (cache_dtype == kBF16 && head_dim == 64) return launch_t<kBF16, 64, CAS>(a, stream);
-    if (cache_dtype == kBF16 && head_dim == 128) return launch_t<kBF16, 128, CAS>(a, stream);
-    if (cache_dtype == kFP8 && head_dim == 64) return launch_t<kFP8, 64, CAS>(a, stream);
-    if (cache_dtype == kFP8 && head_dim == 128) return launch_t<kFP8, 128, CAS>(a, stream);
+    if (cache_dtype == kF32 && head_dim == 64) return launch_t<kF32, 64, M>(a, stream);
+    if (cache_dtype == kF32 && head_dim == 128) return launch_t<kF32, 128, M>(a, stream);
+    if (cache_dtype == kBF16 && head_dim == 64) return launch_t<kBF16, 64, M>(a, stream);
+    if (cache_dtype == kBF16 && head_dim == 128) return launch_t<kBF16, 128, M>(a, stream);
+    if (cache_dtype == kFP8 && head_dim == 64) return launch_t<kFP8, 64, M>(a, stream);
+    if (cache_dtype == kFP8 && head_dim == 128) return launch_t<kFP8, 128, M>(a, stream);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    return a.prefix_leader ? launch_c<true>(cache_dtype, head_dim, a, stream)
-                           : launch_c<false>(cache_dtype, head_dim, a, stream);
+    if (a.cu_q) return launch_c<kModeMulti>(cache_dtype, head_dim, a, stream);
+    if (a.prefix_leader) return launch_c<kModeShared>(cache_dtype, head_dim, a, stream);
+    return launch_c<kModePlain>(cache_dtype, head_dim, a, stream);
 }
 
 }  // namespace pkv

@@ -108,9 +108,16 @@ struct DecodeArgs {
     int32_t* meet;                 // [num_seqs * runs] arrival counters of prefix and suffix states (workspace)
     float* pstate;                 // [num_seqs * num_heads] state rows of the prefix part
     float* sstate;                 // [num_seqs * num_heads] state rows of the suffix part
-    int32_t members;               // sequences whose heads share one prefix run's columns
+    int32_t members;               // sequences (shared prefix) or new tokens (several queries) per run's columns
     int32_t state_bytes;           // bytes of pstate (and of sstate)
+    // several new query tokens per sequence only (null / 0 otherwise)
+    const int32_t* cu_q;           // [num_seqs + 1] first query row of each sequence
+    int32_t num_q_rows;            // rows of q and out
 };
+
+// What the decode kernel computes: one query token per sequence, the same
+// with shared prefixes read once, or several new query tokens per sequence.
+enum Mode : int { kModePlain = 0, kModeShared = 1, kModeMulti = 2 };
 
 // Shared-prefix state rows, after the slots: two arrays (prefix, suffix) of
 // num_seqs * num_heads rows (row = sequence * num_heads + head) of head_dim + 4

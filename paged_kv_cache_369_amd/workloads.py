@@ -89,6 +89,7 @@ class Workload:
     block_size: int = BLOCK_SIZE
     prefix_leader: Optional[np.ndarray] = None  # [B] int32 first sequence of each sharing group
     prefix_blocks: Optional[np.ndarray] = None  # [B] int32 leading blocks the group shares
+    cu_q: Optional[np.ndarray] = None           # [B + 1] int32 query rows per sequence (several new tokens)
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -446,6 +447,56 @@ def make_shared(name: str, seed: int, groups, num_heads: int, num_kv_heads: int,
     if cache_dtype == "fp8":
         w.k_scale = float(np.float32(_amax([pk, ok_], in_dtype)) / np.float32(448.0))
         w.v_scale = float(np.float32(_amax([pv, ov_], in_dtype)) / np.float32(448.0))
+    return w
+
+
+def make_multi(name: str, seed: int, lens, new_tokens, num_heads: int, num_kv_heads: int, head_dim: int,
+               q_dtype: str, cache_dtype: str, in_dtype: Optional[str] = None, partition_size: int = 0,
+               pool_factor: float = 1.0) -> Workload:
+    """Several new tokens per sequence (a chunk of a prompt, or speculated tokens to verify).
+
+    Sequence s caches lens[s] tokens; its last new_tokens[s] are this step's new tokens (written through
+    slot_mapping in the step, ``layout.new_slots`` / ``new_k`` / ``new_v``, one row per new token), the rest
+    are history.  q holds one row per new token, sequence by sequence; cu_q [B + 1] gives the rows."""
+    lens = np.asarray(lens, dtype=np.int32)
+    nnew = np.asarray(new_tokens, dtype=np.int32)
+    if np.any(nnew < 0) or np.any(nnew > lens):
+        raise ValueError("each sequence needs 0 <= new tokens <= cached tokens")
+    if in_dtype is None:
+        in_dtype = q_dtype if cache_dtype == "fp8" else cache_dtype
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(0,))))
+    need = int(sum(blocks_for(L) for L in lens))
+    pool = max(int(math.ceil(need * pool_factor)), need, 1)
+    mb = max([blocks_for(L) for L in lens] + [1])
+    bt = _private_layout(rng, lens, pool, mb)
+    total = int(lens.sum())
+    k_all = _values(seed, 2, (total, num_kv_heads, head_dim), in_dtype)
+    v_all = _values(seed, 3, (total, num_kv_heads, head_dim), in_dtype)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    hist_idx, hist_slots, new_idx, new_slots = [], [], [], []
+    for s_, L in enumerate(lens.tolist()):
+        n = int(nnew[s_])
+        pos_h = np.arange(L - n, dtype=np.int64)
+        pos_n = np.arange(L - n, L, dtype=np.int64)
+        hist_idx.append(starts[s_] + pos_h)
+        hist_slots.append(_slots_for(bt[s_], pos_h))
+        new_idx.append(starts[s_] + pos_n)
+        new_slots.append(_slots_for(bt[s_], pos_n))
+    hi = np.concatenate(hist_idx).astype(np.int64)
+    ni = np.concatenate(new_idx).astype(np.int64)
+    hist = WriteBatch(np.ascontiguousarray(k_all[hi]), np.ascontiguousarray(v_all[hi]),
+                      np.concatenate(hist_slots).astype(np.int32))
+    cu = np.concatenate([[0], np.cumsum(nnew)]).astype(np.int32)
+    q = _values(seed, 1, (int(cu[-1]), num_heads, head_dim), q_dtype)
+    w = Workload(name=name, num_seqs=len(lens), num_heads=num_heads, num_kv_heads=num_kv_heads,
+                 head_dim=head_dim, q_dtype=q_dtype, in_dtype=in_dtype, cache_dtype=cache_dtype, context_lens=lens,
+                 q=q, new_k=np.ascontiguousarray(k_all[ni]), new_v=np.ascontiguousarray(v_all[ni]),
+                 layout=Layout(pool, bt, [hist], np.concatenate(new_slots).astype(np.int32)),
+                 scale=float(np.float32(1.0) / np.sqrt(np.float32(head_dim))), partition_size=partition_size,
+                 cu_q=cu)
+    if cache_dtype == "fp8":
+        w.k_scale = float(np.float32(_amax([k_all], in_dtype)) / np.float32(448.0))
+        w.v_scale = float(np.float32(_amax([v_all], in_dtype)) / np.float32(448.0))
     return w
 
 

@@ -121,3 +121,19 @@ def gpu_decode_cascade(w: W.Workload, layout: W.Layout, kp, vp, prefix_leader=No
                                        w.scale, w.k_scale, w.v_scale, partition_size=part, workspace=workspace)
     torch.cuda.synchronize()
     return widen(to_host(out, w.q_dtype), w.q_dtype)
+
+
+def gpu_varlen(w: W.Workload, layout: W.Layout, kp, vp, partition_size=None, cu=None, out=None, workspace=None):
+    q_dev = to_dev(w.q, w.q_dtype)
+    o = torch.empty_like(q_dev) if out is None else out
+    part = w.partition_size if partition_size is None else partition_size
+    pkv.paged_attention_varlen(o, q_dev, to_dev(w.cu_q if cu is None else cu, "i32"), kp, vp,
+                               to_dev(layout.block_table, "i32"), to_dev(w.context_lens, "i32"), w.scale,
+                               w.k_scale, w.v_scale, partition_size=part, workspace=workspace)
+    torch.cuda.synchronize()
+    return widen(to_host(o, w.q_dtype), w.q_dtype)
+
+
+def oracle_varlen(w: W.Workload, layout: W.Layout, kp, vp):
+    return oracle.paged_attention_varlen(w.q, w.q_dtype, w.cu_q, kp, vp, w.cache_dtype, layout.block_table,
+                                         w.context_lens, w.scale, w.k_scale, w.v_scale)

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 5
+    assert lib.pkv_abi_version() == 6
     for st in range(7):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -179,3 +179,28 @@ def test_cascade_validation_and_workspace(lib):
     assert _cas(lib, wsb=need - 1) == WORKSPACE
     assert _cas(lib, wsb=lib.paged_attention_workspace_bytes(4, 32, 8, 128, 64, 16, 0)) == WORKSPACE
     assert _cas(lib, B=0) == OK
+
+
+def _var(lib, **kw):
+    a = dict(out=A, q=A, qd=1, cu=A, T=64, kc=A, vc=A, cd=1, bt=A, MB=64, cl=A, B=4, H=32, Hkv=8, D=128, bs=16,
+             NB=300, scale=0.088, ks=1.0, vs=1.0, part=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return lib.paged_attention_varlen(a["out"], a["q"], a["qd"], a["cu"], a["T"], a["kc"], a["vc"], a["cd"], a["bt"],
+                                      a["MB"], a["cl"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"],
+                                      a["ks"], a["vs"], a["part"], a["ws"], a["wsb"], None)
+
+
+def test_varlen_validation_and_workspace(lib):
+    vws = lib.paged_attention_varlen_workspace_bytes
+    assert vws(4, 32, 8, 128, 64, 16, 0) == _ws(16, 128)       # 4 tokens x 4 heads per run
+    assert vws(4, 64, 8, 128, 64, 16, 0) == _ws(16, 128)       # 2 tokens x 8 heads
+    assert vws(4, 24, 2, 64, 64, 16, 0) == _ws(12, 64)         # 1 token x 12 heads
+    assert vws(2, 8, 3, 64, 10, 16, 0) == 0
+    assert _var(lib, cu=0) == INVALID
+    assert _var(lib, T=-1) == INVALID
+    assert _var(lib, cu=A + 2) == ALIGN
+    assert _var(lib, qd=0, cd=1) == UNSUPPORTED
+    assert _var(lib, T=1 << 20, H=64, D=128) == UNSUPPORTED     # rows * heads * head_dim reach 2^31
+    assert _var(lib, wsb=vws(4, 32, 8, 128, 64, 16, 0) - 1) == WORKSPACE
+    assert _var(lib, T=0) == OK
+    assert _var(lib, B=0) == OK
