@@ -55,6 +55,8 @@ WORKLOAD_DESC = {
     "13b": "LLaMA-2-13B-shaped bf16 decode: B=64, 40/40 heads, D=128, lens U[128,2048]",
     "gqa8b": "Llama-3-8B-shaped GQA bf16 decode: B=256, 32 q / 8 kv heads, D=128, lens log-U[256,8192]",
     "prefix": "shared-prefix bf16 decode: 32 prompts x 8 samples, 32/8 heads, D=128, 1024-token aliased prefix",
+    "spec4": "speculative verification: the gqa8b batch with 4 new query tokens per sequence (1024 rows), bf16",
+    "chunk512": "chunked prefill: 16 sequences x 512 new tokens on contexts U[2048, 8192], 32/8 heads, D=128, bf16",
     "longfp8": "long-context fp8-e4m3 KV decode: B=16, 64 q / 8 kv heads, D=128, lens U[16384,32768], 512-token partitions",
 }
 # Sources whose change invalidates counter figures taken on the decode call.
@@ -110,6 +112,20 @@ def cascade_read_bytes(w) -> int:
             tokens += pb * 16
         tokens += L - pb * 16
     return tokens * w.num_kv_heads * w.head_dim * 2 * w.kv_elt_bytes()
+
+
+def varlen_read_bytes(w) -> int:
+    """KV bytes paged_attention_varlen reads: every group of 16 / run_heads new tokens of a sequence reads its
+    context up to the group's last token, once per run of query heads."""
+    rh = run_heads(w.num_heads // w.num_kv_heads)
+    tpr = 16 // rh
+    runs = w.num_heads // rh
+    tokens = 0
+    for s, L in enumerate(w.context_lens.tolist()):
+        n = int(w.cu_q[s + 1] - w.cu_q[s])
+        for g in range(0, n, tpr):
+            tokens += L - n + min(g + tpr, n)
+    return tokens * runs * w.head_dim * 2 * w.kv_elt_bytes()
 
 
 def profile_key(args) -> str:
@@ -201,7 +217,8 @@ def _pick(per_kernel, key):
 # Longest context each workload's length law allows: what a contiguous allocator must reserve per sequence.
 CASCADE_NOTE = ", decoded by paged_attention_decode_cascade (each shared prefix read once per chunk of samples)"
 
-MAX_LEN = {"tiny": 100, "13b": 2048, "gqa8b": 8192, "prefix": 1024 + 512, "longfp8": 32768}
+MAX_LEN = {"tiny": 100, "13b": 2048, "gqa8b": 8192, "prefix": 1024 + 512, "longfp8": 32768, "spec4": 8192,
+           "chunk512": 8192}
 
 
 def utilisation_rows():
@@ -362,19 +379,33 @@ def oracle_baseline(w, out_dev, q_dtype, max_seqs: int):
         oracle.kv_write(b.k, b.v, w.in_dtype, kp, vp, w.cache_dtype, b.slots, k_scale=w.k_scale, v_scale=w.v_scale)
     oracle.kv_write(w.new_k, w.new_v, w.in_dtype, kp, vp, w.cache_dtype, w.layout.new_slots,
                     k_scale=w.k_scale, v_scale=w.v_scale)
-    n = w.num_seqs if max_seqs < 0 else min(max_seqs, w.num_seqs)
+    if max_seqs < 0:  # the longest prefix of sequences within about 4e9 query-row x token x head x dim products
+        rows_per = np.diff(w.cu_q) if w.cu_q is not None else np.ones(w.num_seqs, dtype=np.int64)
+        cost = np.cumsum(rows_per.astype(np.float64) * w.context_lens * w.num_heads * w.head_dim)
+        n = max(1, int(np.searchsorted(cost, 4e9, side="right")))
+        n = min(n, w.num_seqs)
+    else:
+        n = min(max_seqs, w.num_seqs)
     sl = slice(0, n)
     t0 = time.perf_counter()
-    ref = oracle.paged_attention(np.ascontiguousarray(w.q[sl]), w.q_dtype, kp, vp, w.cache_dtype,
-                                 np.ascontiguousarray(w.layout.block_table[sl]),
-                                 np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
+    if w.cu_q is not None:  # several new tokens per sequence: the rows of the first n sequences
+        rows = int(w.cu_q[n])
+        ref = oracle.paged_attention_varlen(np.ascontiguousarray(w.q[:rows]), w.q_dtype,
+                                            np.ascontiguousarray(w.cu_q[:n + 1]), kp, vp, w.cache_dtype,
+                                            np.ascontiguousarray(w.layout.block_table[sl]),
+                                            np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
+    else:
+        rows = n
+        ref = oracle.paged_attention(np.ascontiguousarray(w.q[sl]), w.q_dtype, kp, vp, w.cache_dtype,
+                                     np.ascontiguousarray(w.layout.block_table[sl]),
+                                     np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
     dt = time.perf_counter() - t0
     import torch
-    o = out_dev[:n].detach().cpu()
+    o = out_dev[:rows].detach().cpu()
     got = (o.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32) \
         if q_dtype == "bf16" else o.numpy()
     err = float(np.max(np.abs(got.astype(np.float64) - ref))) if ref.size else 0.0
-    return n, dt, oracle.num_threads(0), err
+    return n, rows, dt, oracle.num_threads(0), err
 
 
 def main() -> int:
@@ -386,7 +417,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1 = the workload's setting (0 = balanced split only)")
     ap.add_argument("--cpu-seqs", type=int, default=-1,
-                    help="sequences in the CPU-oracle baseline and check (-1 = all, 0 = skip)")
+                    help="sequences in the CPU-oracle baseline and check (-1 = as many as fit about 4e9 "
+                         "multiply-adds: every sequence of the decode workloads; 0 = skip)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cascade", action="store_true",
                     help="decode with paged_attention_decode_cascade using the workload's sharing arrays")
@@ -443,6 +475,7 @@ def main() -> int:
     if args.cascade and w.prefix_leader is None:
         print(f"workload {args.workload} declares no shared prefixes", file=sys.stderr)
         return 2
+    multi = w.cu_q is not None  # several new query tokens per sequence
 
     # device-resident inputs
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
@@ -460,12 +493,15 @@ def main() -> int:
     out = torch.empty_like(q)
     bt = _dev(layout.block_table, "i32", torch)
     cl = _dev(w.context_lens, "i32", torch)
-    ws_query = pkv.paged_attention_cascade_workspace_bytes if args.cascade else pkv.paged_attention_workspace_bytes
+    ws_query = (pkv.paged_attention_cascade_workspace_bytes if args.cascade else
+                pkv.paged_attention_varlen_workspace_bytes if multi else pkv.paged_attention_workspace_bytes)
     ws_bytes = ws_query(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq, W.BLOCK_SIZE,
                         part)
     if args.cascade:
         pl = _dev(w.prefix_leader, "i32", torch)
         pbl = _dev(w.prefix_blocks, "i32", torch)
+    if multi:
+        cuq = _dev(w.cu_q, "i32", torch)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
@@ -476,6 +512,9 @@ def main() -> int:
         if args.cascade:
             pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, pl, pbl, w.scale, w.k_scale, w.v_scale,
                                                partition_size=part, workspace=ws)
+        elif multi:
+            pkv.paged_attention_varlen(out, q, cuq, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
+                                       partition_size=part, workspace=ws)
         else:
             pkv.paged_attention_decode(out, q, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
                                        partition_size=part, workspace=ws)
@@ -515,7 +554,8 @@ def main() -> int:
     t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     dec_us = float(np.mean(t_dec))
-    kv_bytes = cascade_read_bytes(w) if args.cascade else w.kv_bytes()
+    kv_bytes = cascade_read_bytes(w) if args.cascade else varlen_read_bytes(w) if multi else w.kv_bytes()
+    rows = int(q.shape[0])  # query tokens per step
     achieved = kv_bytes / (dec_us * 1e-6) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; events: write {np.mean(t_write):.1f} us, "
         f"decode call {dec_us:.1f} us (p10 {np.percentile(t_dec, 10):.1f}, p90 {np.percentile(t_dec, 90):.1f}), "
@@ -526,7 +566,7 @@ def main() -> int:
                 "block_table_bytes": bt.numel() * 4, "context_lens_bytes": cl.numel() * 4}
     result = {
         "metric": "paged-attn decode tokens/s and achieved KV-read GB/s (% HBM peak), 1 GPU",
-        "value": w.num_seqs / (ms_per_step * 1e-3),
+        "value": rows / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -542,8 +582,9 @@ def main() -> int:
                    "block_size": W.BLOCK_SIZE, "kv_dtype": w.cache_dtype, "q_dtype": w.q_dtype,
                    "sum_context": int(w.context_lens.sum()),
                    "partition_size": part, "kv_bytes": kv_bytes, "kv_unique_bytes": w.kv_unique_bytes(),
-                   "kv_logical_bytes": w.kv_bytes(), "mall_flush": args.flush_mall,
-                   "decode": "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"},
+                   "kv_logical_bytes": w.kv_bytes(), "mall_flush": args.flush_mall, "query_rows": rows,
+                   "decode": ("paged_attention_decode_cascade" if args.cascade else
+                              "paged_attention_varlen" if multi else "paged_attention_decode")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
@@ -552,19 +593,19 @@ def main() -> int:
                      "avg_us": dec_us,
                      "algorithmic_bytes_per_call": kv_bytes},
         "write_us": float(np.mean(t_write)),
-        "attention_tokens_per_s": w.num_seqs / (dec_us * 1e-6),
+        "attention_tokens_per_s": rows / (dec_us * 1e-6),
         "overhead_bytes": overhead,
         "cpu_baseline": None,
         "check": None,
     }
 
     if args.cpu_seqs != 0:
-        n, dt, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)
+        n, nrows, dt, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)
         tok = int(w.context_lens[:n].sum())
         result["cpu_baseline"] = {
-            "value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.num_seqs} sequences of this workload (all {w.num_heads} heads, {tok} context "
-                      f"tokens, one decode step), {dt:.2f} s wall on {cores} threads of {cpu_model()}",
+            "value": nrows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.num_seqs} sequences of this workload ({nrows} query tokens, all {w.num_heads} "
+                      f"heads, {tok} context tokens, one step), {dt:.2f} s wall on {cores} threads of {cpu_model()}",
         }
         result["check"] = {"max_abs_err_vs_oracle": err, "tolerance": TOL[w.cache_dtype], "seqs": n,
                            "pass": bool(err <= TOL[w.cache_dtype])}

@@ -22,6 +22,12 @@ block size 16 from the ipipp.com vLLM article, section 二):
   longfp8  B=16, 64 query / 8 KV heads, D=128, fp8-e4m3 cache with one fp32
            scale per pool, bf16 Q and new K/V, lengths uniform in
            [16384, 32768], 512-token partitions.
+  spec4    the gqa8b batch verifying speculated tokens: 4 new query tokens
+           per sequence (3 guesses and the token before them), lengths as
+           gqa8b counting the new tokens.
+  chunk512 chunked prefill: 16 sequences, 32/8 heads, D=128, bf16, each
+           taking a 512-token chunk of its prompt, contexts (chunk included)
+           uniform in [2048, 8192].
 
 Values: N(0, 1) drawn as float32 from PCG64 sub-streams of fixed size (so
 the bytes do not depend on the thread count), then cast to bf16 with torch's
@@ -45,7 +51,7 @@ import numpy as np
 BLOCK_SIZE = 16
 CHUNK = 1 << 22  # values per PCG64 sub-stream
 
-WORKLOADS = ("tiny", "13b", "gqa8b", "prefix", "longfp8")
+WORKLOADS = ("tiny", "13b", "gqa8b", "prefix", "longfp8", "spec4", "chunk512")
 SEEDS = {name: 20260000 + i for i, name in enumerate(WORKLOADS)}
 
 
@@ -278,6 +284,11 @@ def _lens_for(name: str, rng: np.random.Generator) -> np.ndarray:
         return np.clip(np.floor(np.exp(u)), 256, 8192).astype(np.int32)
     if name == "longfp8":
         return rng.integers(16384, 32768, size=16, endpoint=True).astype(np.int32)
+    if name == "spec4":
+        u = rng.uniform(np.log(256.0), np.log(8192.0), size=256)
+        return np.clip(np.floor(np.exp(u)), 256, 8192).astype(np.int32)
+    if name == "chunk512":
+        return rng.integers(2048, 8192, size=16, endpoint=True).astype(np.int32)
     raise ValueError(name)
 
 
@@ -527,6 +538,10 @@ def make(name: str, seed: Optional[int] = None) -> Workload:
     if name == "longfp8":
         return make_custom("longfp8", seed, lens, 64, 8, 128, "bf16", "fp8", max_blocks_per_seq=2048,
                            partition_size=512, in_dtype="bf16")
+    if name == "spec4":
+        return make_multi("spec4", seed, lens, [4] * len(lens), 32, 8, 128, "bf16", "bf16")
+    if name == "chunk512":
+        return make_multi("chunk512", seed, lens, [512] * len(lens), 32, 8, 128, "bf16", "bf16")
     raise ValueError(name)
 
 
