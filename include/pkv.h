@@ -76,7 +76,7 @@ typedef enum pkv_status {
  * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
  * use and is left that way by every call; 4 = the block manager and
  * paged_kv_copy_blocks; 5 = paged_attention_decode_cascade; 6 =
- * paged_attention_varlen). */
+ * paged_attention_varlen; 7 = the block manager's prefix caching). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -400,6 +400,49 @@ int32_t pkv_bm_take_copies(pkv_block_manager* m, int32_t* src_out, int32_t* dst_
 /* out (host int64[5]): free blocks, used blocks, live sequences, tokens held
  * by the used blocks (a shared block counted once), pending copies. */
 int pkv_bm_stats(const pkv_block_manager* m, int64_t* out);
+
+/*
+ * Automatic prefix caching (off unless enabled).
+ *   Source: bytelighting wiki "vLLM", paragraph on Automatic Prefix Caching
+ *   (a prefix is cut into fixed blocks; each block's hash chains its parent's
+ *   hash and its own content; cached blocks live in a hash table, are
+ *   allocated, freed and LRU-evicted on their own; a hit matches block by
+ *   block exactly and reuses only full blocks); ai-maas.com article, 引擎的分
+ *   层结构 (repeated prefixes such as system prompts are computed once and
+ *   shared).
+ *
+ * pkv_bm_enable_prefix_caching: turn caching on for an empty manager (no
+ *   sequences, no pending copies); PKV_ERR_INVALID_ARG otherwise.  From then
+ *   on every block a sequence with known token ids fills is registered under
+ *   the chained hash of its content (the parent's hash mixed with the
+ *   block's 16 token ids; a 64-bit mix that only narrows the search), unless
+ *   a block with the same content after the same registered predecessor is
+ *   registered already.  A registered block whose last reference goes is
+ *   kept as evictable; when no never-registered block is free, the
+ *   least recently released evictable block is taken (and unregistered).  A
+ *   freed sequence releases its blocks deepest first.  pkv_bm_stats counts
+ *   evictable blocks as free.
+ * pkv_bm_add_prompt: add sequence seq_id (new) with its n prompt token ids.
+ *   Its first blocks reuse the longest run of registered full blocks that
+ *   match the prompt exactly (token ids, and each block's predecessor), at
+ *   most (n - 1) / 16 blocks, so the last prompt token is always computed.
+ *   *cached_out = the number of reused tokens (a multiple of 16); the slots
+ *   of the other n - *cached_out tokens are written to slots_out, whose K/V
+ *   the caller writes with paged_kv_write.  PKV_ERR_OUT_OF_BLOCKS leaves the
+ *   manager unchanged.
+ * pkv_bm_append_tokens: pkv_bm_append with the new tokens' ids, so the blocks
+ *   they fill can be registered.  (pkv_bm_append without ids stops the
+ *   registration of that sequence's later blocks.)
+ * pkv_bm_cache_stats: out[0] registered blocks, out[1] of them evictable,
+ *   out[2] full prompt blocks looked up, out[3] of them reused, out[4]
+ *   evictions.
+ */
+int pkv_bm_enable_prefix_caching(pkv_block_manager* m);
+int pkv_bm_add_prompt(pkv_block_manager* m, int64_t seq_id, const int32_t* tokens, int32_t n, int32_t* slots_out,
+                      int32_t* cached_out);
+int pkv_bm_append_tokens(pkv_block_manager* m, int64_t seq_id, const int32_t* tokens, int32_t n,
+                         int32_t* slots_out);
+int pkv_bm_cache_stats(const pkv_block_manager* m, int64_t* out);
 
 /*
  * paged_kv_copy_blocks -- copy whole blocks of both pools, K and V of every

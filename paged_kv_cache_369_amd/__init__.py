@@ -93,6 +93,14 @@ def _load():
     lib.pkv_bm_take_copies.restype = i32
     lib.pkv_bm_stats.argtypes = [p, p]
     lib.pkv_bm_stats.restype = ctypes.c_int
+    lib.pkv_bm_enable_prefix_caching.argtypes = [p]
+    lib.pkv_bm_enable_prefix_caching.restype = ctypes.c_int
+    lib.pkv_bm_add_prompt.argtypes = [p, i64, p, i32, p, p]
+    lib.pkv_bm_add_prompt.restype = ctypes.c_int
+    lib.pkv_bm_append_tokens.argtypes = [p, i64, p, i32, p]
+    lib.pkv_bm_append_tokens.restype = ctypes.c_int
+    lib.pkv_bm_cache_stats.argtypes = [p, p]
+    lib.pkv_bm_cache_stats.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [p, p, ctypes.c_int, i32, i32, i32, i32, p, p, i32, p]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     _lib = lib
@@ -355,6 +363,34 @@ class BlockManager:
 
     def free(self, seq: int):
         _check(self._lib.pkv_bm_free(self._h, int(seq)), "pkv_bm_free")
+
+    def enable_prefix_caching(self):
+        _check(self._lib.pkv_bm_enable_prefix_caching(self._h), "pkv_bm_enable_prefix_caching")
+
+    def add_prompt(self, seq: int, tokens):
+        """New sequence with its prompt token ids -> (slots of the tokens to compute, tokens reused)."""
+        import numpy as np
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(len(tok), 1), dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_add_prompt(self._h, int(seq), tok.ctypes.data, len(tok), slots.ctypes.data,
+                                           ctypes.byref(cached)), "pkv_bm_add_prompt")
+        return slots[:len(tok) - cached.value].copy(), cached.value
+
+    def append_tokens(self, seq: int, tokens):
+        import numpy as np
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(len(tok), 1), dtype=np.int32)
+        _check(self._lib.pkv_bm_append_tokens(self._h, int(seq), tok.ctypes.data, len(tok), slots.ctypes.data),
+               "pkv_bm_append_tokens")
+        return slots[:len(tok)].copy()
+
+    def cache_stats(self):
+        """(registered blocks, evictable blocks, prompt blocks looked up, reused, evictions)"""
+        import numpy as np
+        out = np.zeros(5, dtype=np.int64)
+        _check(self._lib.pkv_bm_cache_stats(self._h, out.ctypes.data), "pkv_bm_cache_stats")
+        return tuple(int(x) for x in out)
 
     def table(self, seqs, max_blocks: int):
         import numpy as np

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 6
+    assert lib.pkv_abi_version() == 7
     for st in range(7):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"

@@ -104,3 +104,61 @@ def test_fork_copy_on_write_decode(gpu):
     # the pools agree byte for byte too
     assert np.array_equal(kg.view(torch.int16).cpu().numpy().view(np.uint16), ko)
     assert np.array_equal(vg.view(torch.int16).cpu().numpy().view(np.uint16), vo)
+
+
+def _kv_of_prefix(tokens, hkv, d):
+    """K and V rows (float32) of the last token of `tokens`: a function of the whole prefix, as a model's are."""
+    seed = hash(tuple(int(t) for t in tokens)) & 0x7fffffff
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((hkv, d)).astype(np.float32), rng.standard_normal((hkv, d)).astype(np.float32)
+
+
+def test_prefix_cache_reuse_decodes_like_private_copies(gpu):
+    """Prompts sharing system prefixes go through the manager with prefix caching; only the tokens it does not
+    reuse are written.  Decoding each sequence over its table equals attention over a private copy of its own
+    tokens' K/V (oracle)."""
+    rnd = random.Random(5)
+    hq, hkv, d, nb = 8, 2, 64, 120
+    systems = [[rnd.randint(0, 20) for _ in range(n)] for n in (48, 33, 80)]
+    bm = pkv.BlockManager(nb, 16)
+    bm.enable_prefix_caching()
+    kc = torch.zeros(pkv.k_cache_shape(nb, hkv, d, "f32"), dtype=torch.float32, device="cuda")
+    vc = torch.zeros(pkv.v_cache_shape(nb, hkv, d), dtype=torch.float32, device="cuda")
+    prompts = {}
+    reused = 0
+    for s in range(12):
+        toks = list(rnd.choice(systems)) + [rnd.randint(0, 20) for _ in range(rnd.randint(1, 30))]
+        slots, cached = bm.add_prompt(s, toks)
+        reused += cached
+        prompts[s] = toks
+        kn = np.stack([_kv_of_prefix(toks[:p + 1], hkv, d)[0] for p in range(cached, len(toks))])
+        vn = np.stack([_kv_of_prefix(toks[:p + 1], hkv, d)[1] for p in range(cached, len(toks))])
+        pkv.paged_kv_write(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), kc, vc,
+                           torch.from_numpy(slots.astype(np.int32)).cuda())
+        if s in (3, 7):
+            bm.free(s - 1)             # released blocks stay registered and may be reused or evicted
+            del prompts[s - 1]
+    assert reused > 0
+    seqs = sorted(prompts)
+    tab, lens = bm.table(seqs, 16)
+    q = np.random.default_rng(9).standard_normal((len(seqs), hq, d)).astype(np.float32)
+    out = torch.empty((len(seqs), hq, d), dtype=torch.float32, device="cuda")
+    _gpu.note("prefix cache reuse decode")
+    pkv.paged_attention_decode(out, torch.from_numpy(q).cuda(), kc, vc, torch.from_numpy(tab).cuda(),
+                               torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(), 0.125)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # oracle: each sequence's own tokens in a private pool
+    priv_tab = np.full((len(seqs), 16), -1, dtype=np.int32)
+    kp = np.zeros(oracle.k_pool_shape(len(seqs) * 16, hkv, d, "f32"), dtype=np.float32)
+    vp = np.zeros(oracle.v_pool_shape(len(seqs) * 16, hkv, d, "f32"), dtype=np.float32)
+    for r, s in enumerate(seqs):
+        toks = prompts[s]
+        nblk = -(-len(toks) // 16)
+        priv_tab[r, :nblk] = np.arange(r * 16, r * 16 + nblk)
+        kk = np.stack([_kv_of_prefix(toks[:p + 1], hkv, d)[0] for p in range(len(toks))])
+        vv = np.stack([_kv_of_prefix(toks[:p + 1], hkv, d)[1] for p in range(len(toks))])
+        sl = np.array([priv_tab[r, p // 16] * 16 + p % 16 for p in range(len(toks))], dtype=np.int32)
+        oracle.kv_write(kk, vv, "f32", kp, vp, "f32", sl)
+    want = oracle.paged_attention(q, "f32", kp, vp, "f32", priv_tab, np.asarray(lens, dtype=np.int32), 0.125)
+    assert np.max(np.abs(got - want)) <= _gpu.TOL["f32"]
