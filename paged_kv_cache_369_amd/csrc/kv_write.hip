@@ -9,12 +9,13 @@
 // elements), and the V pool is dimension-major ([d][offset]) -- the layouts
 // the decode kernel's matrix-core operands load directly.
 //
-// One thread per 16-byte K chunk of a (token, head) row: consecutive threads
-// take consecutive chunks and then consecutive heads, so the reads of the new
-// tokens are fully coalesced and every K store is one aligned 16-byte write.
-// The same thread scatters the chunk's dimensions into the V tile (one element
-// per dimension row).  The fp8 variant reads 16 input elements per thread and
-// quantises them with a bit-exact round-to-nearest-even, saturating E4M3
+// One workgroup per group of consecutive new tokens and one KV head.  K
+// chunks are loaded along the token rows (coalesced) and stored as aligned
+// 16-byte writes.  V rows go through LDS, transposed to the pool's
+// dimension-major order, and tokens whose slots are consecutive inside a block
+// (a sequence writing several tokens) are stored as 16-byte pieces of each
+// dimension row; any other token's V elements are stored one by one.  The fp8
+// variant quantises with a bit-exact round-to-nearest-even, saturating E4M3
 // encoder.
 #include <algorithm>
 
@@ -79,81 +80,149 @@ __device__ __forceinline__ void store_chunk(uint8_t* p, uint4 v) {
     __builtin_nontemporal_store(nt_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4*>(p));
 }
 
-// Copy (same dtype): one 16-byte chunk (X elements) per thread.  D = head_dim.
-template <int ELT, int D>
-__global__ __launch_bounds__(256) void kv_copy_kernel(const uint8_t* __restrict__ k_new,
-                                                      const uint8_t* __restrict__ v_new,
-                                                      uint8_t* __restrict__ k_cache,
-                                                      uint8_t* __restrict__ v_cache,
-                                                      const int32_t* __restrict__ slots,
-                                                      int64_t total_chunks, int num_kv_heads, int num_slots) {
-    constexpr int ROW = D * ELT;
-    constexpr int CH = ROW / 16;
-    constexpr int X = 16 / ELT;
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= total_chunks) return;
-    const int c = int(idx % CH);
-    const int64_t th = idx / CH;                 // token * heads + head
-    const int h = int(th % num_kv_heads);
-    const int64_t tok = th / num_kv_heads;
-    const int sl = slots[tok];
-    if (sl < 0 || sl >= num_slots) return;
-    const int64_t src = th * ROW + c * 16;
-    const uint4 kx = *reinterpret_cast<const uint4*>(k_new + src);
-    const uint4 vx = *reinterpret_cast<const uint4*>(v_new + src);
-    store_chunk(k_cache + k_chunk_offset(sl, h, c, num_kv_heads, CH), kx);
-    const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+// One 16-byte chunk of cache elements from X = 16 / CELT input elements at
+// `src` (copied when the input is the cache dtype, else E4M3-quantised).
+template <int IN, int CT>
+__device__ __forceinline__ uint4 cache_chunk(const uint8_t* src, float scale) {
+    if constexpr (IN == CT) {
+        return *reinterpret_cast<const uint4*>(src);
+    } else {
+        uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < X; ++e) {
-        const int64_t dst = v_elem_offset(sl, h, c * X + e, num_kv_heads, D, ELT);
-        if constexpr (ELT == 4) {
-            __builtin_nontemporal_store(w[e], reinterpret_cast<uint32_t*>(v_cache + dst));
-        } else if constexpr (ELT == 2) {
-            __builtin_nontemporal_store(uint16_t(w[e / 2] >> (16 * (e % 2))), reinterpret_cast<uint16_t*>(v_cache + dst));
-        } else {
-            __builtin_nontemporal_store(uint8_t(w[e / 4] >> (8 * (e % 4))), v_cache + dst);
+        for (int i = 0; i < 4; ++i) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b |= e4m3_encode(load_elem<IN>(src, i * 4 + e) / scale) << (8 * e);
+            w[i] = b;
         }
+        return make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-// Quantise: 16 output codes (one 16-byte K chunk) per thread.  D = head_dim.
-template <int IN, int D>
-__global__ __launch_bounds__(256) void kv_quant_kernel(const uint8_t* __restrict__ k_new,
+// A group of kGroup consecutive tokens of one KV head per workgroup.
+//  1. The slots of the group, with CW - 1 tokens of context on each side
+//     (CW = 16 / CELT tokens fill 16 bytes of a dimension row of the V tile).
+//  2. Every K chunk of the group's tokens is loaded (coalesced along the
+//     token rows), converted and stored as one 16-byte write; the group's V
+//     rows (and the next CW - 1 tokens') are converted and transposed into
+//     LDS, dimension-major.
+//  3. A token is *covered* when the CW tokens around it whose slots would
+//     fill its aligned 16-byte piece of the dimension rows (slot % CW == 0 ..
+//     CW - 1) really hold those consecutive slots -- the usual case when a
+//     sequence writes several new tokens (prefill chunks, speculative tokens).
+//     The first token of such a piece (its head) writes each dimension's
+//     piece as one 16-byte store; the group holding the head writes it.
+//  4. Tokens that are not covered store their elements one by one.
+// Every element of a token with a valid slot is written exactly once, by
+// step 2 (K), 3 or 4 (V).
+constexpr int kGroup = 64;
+
+template <int IN, int CT, int D>
+__global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict__ k_new,
                                                        const uint8_t* __restrict__ v_new,
                                                        uint8_t* __restrict__ k_cache,
                                                        uint8_t* __restrict__ v_cache,
                                                        const int32_t* __restrict__ slots,
-                                                       int64_t total_chunks, int num_kv_heads, int num_slots,
+                                                       int num_tokens, int num_kv_heads, int num_slots,
                                                        float k_scale, float v_scale) {
-    constexpr int CH = D / 16;
-    constexpr int IN_ELT = IN == kF32 ? 4 : 2;
-    constexpr int IN_ROW = D * IN_ELT;
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= total_chunks) return;
-    const int c = int(idx % CH);
-    const int64_t th = idx / CH;
-    const int h = int(th % num_kv_heads);
-    const int64_t tok = th / num_kv_heads;
-    const int sl = slots[tok];
-    if (sl < 0 || sl >= num_slots) return;
-    const uint8_t* ks = k_new + th * IN_ROW + c * 16 * IN_ELT;
-    const uint8_t* vs = v_new + th * IN_ROW + c * 16 * IN_ELT;
-    uint32_t kw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t kb = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kb |= e4m3_encode(load_elem<IN>(ks, w * 4 + e) / k_scale) << (8 * e);
-        kw[w] = kb;
-    }
-    store_chunk(k_cache + k_chunk_offset(sl, h, c, num_kv_heads, CH), make_uint4(kw[0], kw[1], kw[2], kw[3]));
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-        __builtin_nontemporal_store(uint8_t(e4m3_encode(load_elem<IN>(vs, e) / v_scale)),
-                                    v_cache + v_elem_offset(sl, h, c * 16 + e, num_kv_heads, D, 1));
-}
+    constexpr int IELT = IN == kF32 ? 4 : (IN == kBF16 ? 2 : 1);
+    constexpr int CELT = CT == kF32 ? 4 : (CT == kBF16 ? 2 : 1);
+    constexpr int X = 16 / CELT;        // cache elements per 16-byte chunk (= CW)
+    constexpr int CW = X;
+    constexpr int CH = D / X;           // K chunks per token row
+    constexpr int HALO = CW - 1;
+    constexpr int NSL = kGroup + 2 * HALO;  // slots: [t0 - HALO, t0 + kGroup + HALO)
+    constexpr int NVT = kGroup + HALO;      // V tokens held: [t0, t0 + kGroup + HALO)
+    constexpr int PITCH = NVT * CELT;       // bytes of one dimension row in LDS
+    __shared__ int sl[NSL];
+    __shared__ int heads[kGroup];
+    __shared__ int nheads;
+    __shared__ uint8_t kind[kGroup];  // 0: no slot, 1: element stores, 2: head of a piece, 3: inside a piece
+    __shared__ __align__(16) uint8_t vt[D * PITCH];
 
-inline unsigned grid_for(int64_t n) { return unsigned((n + 255) / 256); }
+    const int t0 = int(blockIdx.x) * kGroup;
+    const int h = int(blockIdx.y);
+    const int tid = int(threadIdx.x);
+    // 1. slots (-1: none, past the batch, or outside the pool)
+    for (int i = tid; i < NSL; i += 256) {
+        const int tok = t0 - HALO + i;
+        const int s = (tok >= 0 && tok < num_tokens) ? slots[tok] : -1;
+        sl[i] = (s >= 0 && s < num_slots) ? s : -1;
+    }
+    __syncthreads();
+    // 2. K chunks of the group's tokens; V chunks of the group's tokens and the halo after it
+    const int nv = min(NVT, num_tokens - t0);
+    for (int i = tid; i < nv * CH; i += 256) {
+        const int tt = i / CH, c = i % CH;
+        const int64_t row = int64_t(t0 + tt) * num_kv_heads + h;
+        const int64_t src = (row * D + c * X) * IELT;
+        const int s = sl[tt + HALO];
+        if (tt < kGroup && s >= 0)
+            store_chunk(k_cache + k_chunk_offset(s, h, c, num_kv_heads, CH), cache_chunk<IN, CT>(k_new + src, k_scale));
+        const uint4 vx = cache_chunk<IN, CT>(v_new + src, v_scale);
+        const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+        for (int e = 0; e < X; ++e) {
+            uint8_t* dst = vt + (c * X + e) * PITCH + tt * CELT;
+            if constexpr (CELT == 4) *reinterpret_cast<uint32_t*>(dst) = w[e];
+            else if constexpr (CELT == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w[e / 2] >> (16 * (e % 2)));
+            else *dst = uint8_t(w[e / 4] >> (8 * (e % 4)));
+        }
+    }
+    // 3a. what each token of the group does with its V elements; heads listed in token order
+    if (tid < kGroup) {
+        const int s = sl[tid + HALO];
+        int k = 0;
+        if (s >= 0) {
+            const int e = s % CW;
+            bool cov = true;
+#pragma unroll
+            for (int j = 0; j < CW; ++j) cov = cov && sl[tid - e + j + HALO] == s - e + j;
+            k = cov ? (e == 0 ? 2 : 3) : 1;
+        }
+        kind[tid] = uint8_t(k);
+        const unsigned long long m = __ballot(k == 2);  // kGroup == 64: one wave
+        if (k == 2) heads[__builtin_popcountll(m & ((1ull << tid) - 1))] = tid;
+        if (tid == 0) nheads = __builtin_popcountll(m);
+    }
+    __syncthreads();
+    // 3b. one 16-byte store per (head, dimension); consecutive threads take the
+    // two heads of one block's rows, then the next dimension
+    const int np = (nheads + 1) / 2;
+    for (int i = tid; i < np * 2 * D; i += 256) {
+        const int pr = i / (2 * D), r = i % (2 * D);
+        const int d = r / 2, j = 2 * pr + (r & 1);
+        if (j >= nheads) continue;
+        const int tt = heads[j];
+        const uint8_t* p = vt + d * PITCH + tt * CELT;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (CELT == 4) {
+                w[q] = *reinterpret_cast<const uint32_t*>(p + 4 * q);
+            } else if constexpr (CELT == 2) {
+                w[q] = uint32_t(*reinterpret_cast<const uint16_t*>(p + 4 * q)) |
+                       (uint32_t(*reinterpret_cast<const uint16_t*>(p + 4 * q + 2)) << 16);
+            } else {
+                w[q] = uint32_t(p[4 * q]) | (uint32_t(p[4 * q + 1]) << 8) | (uint32_t(p[4 * q + 2]) << 16) |
+                       (uint32_t(p[4 * q + 3]) << 24);
+            }
+        }
+        store_chunk(v_cache + v_elem_offset(sl[tt + HALO], h, d, num_kv_heads, D, CELT),
+                    make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    // 4. tokens not covered by a piece: one store per element
+    const int ng = min(kGroup, num_tokens - t0);
+    for (int i = tid; i < ng * D; i += 256) {
+        const int tt = i / D, d = i % D;
+        if (kind[tt] != 1) continue;
+        const uint8_t* p = vt + d * PITCH + tt * CELT;
+        uint8_t* dst = v_cache + v_elem_offset(sl[tt + HALO], h, d, num_kv_heads, D, CELT);
+        if constexpr (CELT == 4) __builtin_nontemporal_store(*reinterpret_cast<const uint32_t*>(p), reinterpret_cast<uint32_t*>(dst));
+        else if constexpr (CELT == 2) __builtin_nontemporal_store(*reinterpret_cast<const uint16_t*>(p), reinterpret_cast<uint16_t*>(dst));
+        else __builtin_nontemporal_store(*p, dst);
+    }
+}
 
 }  // namespace
 
@@ -163,30 +232,22 @@ hipError_t launch_kv_write(int in_dtype, int cache_dtype, int head_dim, const Wr
     const auto* vn = static_cast<const uint8_t*>(a.v_new);
     auto* kc = static_cast<uint8_t*>(a.k_cache);
     auto* vc = static_cast<uint8_t*>(a.v_cache);
-    const int64_t rows = int64_t(a.num_tokens) * a.num_kv_heads;
-    if (in_dtype == cache_dtype) {
-        const int64_t n = rows * (head_dim * dtype_bytes(cache_dtype) / 16);
-        const unsigned g = grid_for(n);
-#define PKV_COPY(ELT, D) kv_copy_kernel<ELT, D><<<g, 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots)
-        if (cache_dtype == kF32 && head_dim == 64) PKV_COPY(4, 64);
-        else if (cache_dtype == kF32 && head_dim == 128) PKV_COPY(4, 128);
-        else if (cache_dtype == kBF16 && head_dim == 64) PKV_COPY(2, 64);
-        else if (cache_dtype == kBF16 && head_dim == 128) PKV_COPY(2, 128);
-        else if (cache_dtype == kFP8 && head_dim == 64) PKV_COPY(1, 64);
-        else if (cache_dtype == kFP8 && head_dim == 128) PKV_COPY(1, 128);
-        else return hipErrorInvalidValue;
-#undef PKV_COPY
-    } else {
-        const int64_t n = rows * (head_dim / 16);
-        const unsigned g = grid_for(n);
-#define PKV_QUANT(IN, D) kv_quant_kernel<IN, D><<<g, 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, n, a.num_kv_heads, a.num_slots, a.k_scale, a.v_scale)
-        if (in_dtype == kF32 && head_dim == 64) PKV_QUANT(kF32, 64);
-        else if (in_dtype == kF32 && head_dim == 128) PKV_QUANT(kF32, 128);
-        else if (in_dtype == kBF16 && head_dim == 64) PKV_QUANT(kBF16, 64);
-        else if (in_dtype == kBF16 && head_dim == 128) PKV_QUANT(kBF16, 128);
-        else return hipErrorInvalidValue;
-#undef PKV_QUANT
-    }
+    const dim3 grid(unsigned((a.num_tokens + kGroup - 1) / kGroup), unsigned(a.num_kv_heads));
+#define PKV_WRITE(IN, CT, D)                                                                                         \
+    kv_write_kernel<IN, CT, D><<<grid, 256, 0, stream>>>(kn, vn, kc, vc, a.slot_mapping, a.num_tokens, a.num_kv_heads, \
+                                                         a.num_slots, a.k_scale, a.v_scale)
+    if (in_dtype == cache_dtype && cache_dtype == kF32 && head_dim == 64) PKV_WRITE(kF32, kF32, 64);
+    else if (in_dtype == cache_dtype && cache_dtype == kF32 && head_dim == 128) PKV_WRITE(kF32, kF32, 128);
+    else if (in_dtype == cache_dtype && cache_dtype == kBF16 && head_dim == 64) PKV_WRITE(kBF16, kBF16, 64);
+    else if (in_dtype == cache_dtype && cache_dtype == kBF16 && head_dim == 128) PKV_WRITE(kBF16, kBF16, 128);
+    else if (in_dtype == cache_dtype && cache_dtype == kFP8 && head_dim == 64) PKV_WRITE(kFP8, kFP8, 64);
+    else if (in_dtype == cache_dtype && cache_dtype == kFP8 && head_dim == 128) PKV_WRITE(kFP8, kFP8, 128);
+    else if (in_dtype == kF32 && cache_dtype == kFP8 && head_dim == 64) PKV_WRITE(kF32, kFP8, 64);
+    else if (in_dtype == kF32 && cache_dtype == kFP8 && head_dim == 128) PKV_WRITE(kF32, kFP8, 128);
+    else if (in_dtype == kBF16 && cache_dtype == kFP8 && head_dim == 64) PKV_WRITE(kBF16, kFP8, 64);
+    else if (in_dtype == kBF16 && cache_dtype == kFP8 && head_dim == 128) PKV_WRITE(kBF16, kFP8, 128);
+    else return hipErrorInvalidValue;
+#undef PKV_WRITE
     return hipGetLastError();
 }
 

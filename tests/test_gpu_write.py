@@ -1,4 +1,6 @@
 """GPU parity of paged_kv_write: byte-for-byte equal to the oracle's pools."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -98,3 +100,81 @@ def test_write_empty_is_noop(gpu):
     pkv.paged_kv_write(e, e, kc, vc, torch.empty((0,), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.count_nonzero(kc).item() == 0
+
+
+def _pattern_slots(kind: str, T: int, nb: int, rng) -> np.ndarray:
+    """Slot mappings that exercise the write's 16-byte V pieces and its per-element path."""
+    if kind == "runs":  # each sequence writes consecutive positions starting anywhere in a block
+        out, blocks = [], list(rng.permutation(nb))
+        while len(out) < T:
+            n = int(rng.integers(1, 90))
+            pos = int(rng.integers(0, 16))
+            if not blocks:
+                break
+            while n > 0 and blocks:
+                b = blocks.pop()
+                take = min(n, 16 - pos)
+                out += [b * 16 + pos + i for i in range(take)]
+                n -= take
+                pos = 0
+        return np.array(out[:T], dtype=np.int32)
+    if kind == "holes":  # consecutive slots with skipped tokens and slots past the pool
+        s = np.arange(5, 5 + T, dtype=np.int32)
+        r = rng.random(T)
+        s[r < 0.04] = -1
+        s[(r >= 0.04) & (r < 0.06)] = nb * 16 + 3
+        return s
+    if kind == "scatter":  # one token per sequence: no two tokens share a piece
+        return rng.permutation(nb * 16)[:T].astype(np.int32)
+    if kind == "aligned":  # whole blocks
+        return np.arange(T, dtype=np.int32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("in_dt,cache_dt", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "fp8"),
+                                            ("f32", "fp8"), ("bf16", "fp8")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["runs", "holes", "scatter", "aligned"])
+def test_write_slot_patterns_match_oracle(gpu, in_dt, cache_dt, D, kind):
+    """Tokens with consecutive slots (prefill chunks, several speculative tokens) are
+    written as whole 16-byte pieces of the V rows; any other slot is written on its
+    own.  Both must leave exactly the oracle's bytes, for runs that start and end
+    anywhere in a block and across the 64-token groups of the kernel."""
+    H, NB = 2, 48
+    T = 301 if kind != "aligned" else NB * 16
+    rng = np.random.default_rng(zlib.crc32(f"{in_dt}/{cache_dt}/{D}/{kind}".encode()))
+    slots = _pattern_slots(kind, T, NB, rng)
+    T = slots.size
+    if in_dt == "fp8":
+        k = rng.integers(0, 256, size=(T, H, D), dtype=np.uint8)
+        v = rng.integers(0, 256, size=(T, H, D), dtype=np.uint8)
+    else:
+        k = rng.standard_normal((T, H, D)).astype(np.float32)
+        v = rng.standard_normal((T, H, D)).astype(np.float32)
+        if in_dt == "bf16":
+            k, v = W.to_bf16_bits(k), W.to_bf16_bits(v)
+    ks = vs = 1.0
+    if cache_dt == "fp8" and in_dt != "fp8":
+        ks, vs = 0.0123, 0.0071
+    _gpu.note(f"write pattern {kind} {in_dt}->{cache_dt} D={D} T={T}")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[cache_dt]
+    kc = torch.empty(pkv.k_cache_shape(NB, H, D, cache_dt), dtype=tdt, device="cuda")
+    vc = torch.empty(pkv.v_cache_shape(NB, H, D, cache_dt), dtype=tdt, device="cuda")
+    if cache_dt == "fp8":
+        kc.fill_(0x5A); vc.fill_(0x5A)
+    else:
+        kc.fill_(float("nan")); vc.fill_(float("nan"))
+    pkv.paged_kv_write(_gpu.to_dev(k, in_dt), _gpu.to_dev(v, in_dt), kc, vc, _gpu.to_dev(slots, "i32"), ks, vs)
+    torch.cuda.synchronize()
+    NPD = _gpu.NP[cache_dt]
+    fill = np.uint8(0x5A) if cache_dt == "fp8" else _gpu.POISON[cache_dt]
+    ok = np.full(oracle.k_pool_shape(NB, H, D, cache_dt), fill, dtype=NPD)
+    ov = np.full(oracle.v_pool_shape(NB, H, D, cache_dt), fill, dtype=NPD)
+    # the library skips slots outside the pool; the oracle takes only -1 as "skip"
+    oslots = np.where((slots >= 0) & (slots < NB * 16), slots, -1).astype(np.int32)
+    oracle.kv_write(k, v, in_dt, ok, ov, cache_dt, oslots, k_scale=ks, v_scale=vs)
+    gk, gv = _gpu.to_host(kc, cache_dt), _gpu.to_host(vc, cache_dt)
+    if cache_dt == "f32":  # NaN poison compares by bits
+        gk, gv, ok, ov = gk.view(np.uint32), gv.view(np.uint32), ok.view(np.uint32), ov.view(np.uint32)
+    assert np.array_equal(gk.view(np.uint8), ok.view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), ov.view(np.uint8))
