@@ -48,6 +48,7 @@ if ROOT not in sys.path:
 
 PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 COPY_BYTES = 1 << 30
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
 WORKLOAD_DESC = {
@@ -128,8 +129,30 @@ def varlen_read_bytes(w) -> int:
     return tokens * runs * w.head_dim * 2 * w.kv_elt_bytes()
 
 
+def prefill_flops(w) -> int:
+    """Algorithmic flops of causal attention of every new token over its visible positions: per query row and
+    head, 2 * D per visible position for the scores and 2 * D for the weighted sum of values."""
+    vis = 0
+    for s, L in enumerate(w.context_lens.tolist()):
+        n = int(w.cu_q[s + 1] - w.cu_q[s])
+        vis += n * (L - n) + n * (n + 1) // 2
+    return 4 * w.head_dim * w.num_heads * vis
+
+
+def prefill_read_bytes(w) -> int:
+    """KV bytes the tiled prefill reads from the pools at most: each wave (64 / G new tokens of one sequence and
+    KV head) reads the context up to its last token; waves that share a context on one XCD meet in its L2."""
+    tpw = 64 // (w.num_heads // w.num_kv_heads)
+    tokens = 0
+    for s, L in enumerate(w.context_lens.tolist()):
+        n = int(w.cu_q[s + 1] - w.cu_q[s])
+        for t in range(0, n, tpw):
+            tokens += L - n + min(t + tpw, n)
+    return tokens * w.num_kv_heads * w.head_dim * 2 * w.kv_elt_bytes()
+
+
 def profile_key(args) -> str:
-    return args.workload + ("-cascade" if args.cascade else "")
+    return args.workload + ("-cascade" if args.cascade else "") + ("-prefill" if args.prefill else "")
 
 
 def _dev(a, dtype, torch):
@@ -475,6 +498,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cascade", action="store_true",
                     help="decode with paged_attention_decode_cascade using the workload's sharing arrays")
+    ap.add_argument("--prefill", action="store_true",
+                    help="several-token workloads: time paged_attention_prefill (64-column tiles per wave) "
+                         "instead of paged_attention_varlen")
     ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
                     help="read (or overwrite) 512 MB before every step, outside the timed brackets, so the step's "
                          "KV reads cannot hit what the previous step left in the 256 MB infinity cache")
@@ -529,6 +555,9 @@ def main() -> int:
         print(f"workload {args.workload} declares no shared prefixes", file=sys.stderr)
         return 2
     multi = w.cu_q is not None  # several new query tokens per sequence
+    if args.prefill and not multi:
+        print(f"workload {args.workload} has one query token per sequence; --prefill needs several", file=sys.stderr)
+        return 2
 
     # device-resident inputs
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.cache_dtype]
@@ -555,6 +584,7 @@ def main() -> int:
         pbl = _dev(w.prefix_blocks, "i32", torch)
     if multi:
         cuq = _dev(w.cu_q, "i32", torch)
+        max_q = int(np.max(np.diff(w.cu_q)))
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
@@ -565,6 +595,8 @@ def main() -> int:
         if args.cascade:
             pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, pl, pbl, w.scale, w.k_scale, w.v_scale,
                                                partition_size=part, workspace=ws)
+        elif args.prefill:
+            pkv.paged_attention_prefill(out, q, cuq, kc, vc, bt, cl, w.scale, max_q, w.k_scale, w.v_scale)
         elif multi:
             pkv.paged_attention_varlen(out, q, cuq, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
                                        partition_size=part, workspace=ws)
@@ -607,7 +639,8 @@ def main() -> int:
     t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     dec_us = float(np.mean(t_dec))
-    kv_bytes = cascade_read_bytes(w) if args.cascade else varlen_read_bytes(w) if multi else w.kv_bytes()
+    kv_bytes = (cascade_read_bytes(w) if args.cascade else prefill_read_bytes(w) if args.prefill else
+                varlen_read_bytes(w) if multi else w.kv_bytes())
     rows = int(q.shape[0])  # query tokens per step
     achieved = kv_bytes / (dec_us * 1e-6) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; events: write {np.mean(t_write):.1f} us, "
@@ -637,6 +670,7 @@ def main() -> int:
                    "partition_size": part, "kv_bytes": kv_bytes, "kv_unique_bytes": w.kv_unique_bytes(),
                    "kv_logical_bytes": w.kv_bytes(), "mall_flush": args.flush_mall, "query_rows": rows,
                    "decode": ("paged_attention_decode_cascade" if args.cascade else
+                              "paged_attention_prefill" if args.prefill else
                               "paged_attention_varlen" if multi else "paged_attention_decode")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -651,6 +685,16 @@ def main() -> int:
         "cpu_baseline": None,
         "check": None,
     }
+
+    if args.prefill:
+        # a contraction over the visible positions: priced against the matrix cores' dense bf16 peak
+        fl = prefill_flops(w)
+        tf = fl / (dec_us * 1e-6) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic, "traffic_source": traffic_src,
+                              "kernel": "paged_prefill_kernel (the whole prefill call)", "avg_us": dec_us,
+                              "algorithmic_flops_per_call": fl, "kv_read_bytes_bound": kv_bytes}
+        log(f"prefill: {fl / 1e9:.1f} GFLOP per call -> {tf:.1f} TFLOP/s")
 
     if args.cpu_seqs != 0:
         n, nrows, dt, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)

@@ -302,6 +302,40 @@ int paged_attention_varlen(void* out,
                            void* stream);
 
 /*
+ * paged_attention_prefill -- the same result as paged_attention_varlen, in a
+ * shape for long chunks of new tokens (chunked prefill).  One wave serves 64
+ * query columns -- 64 / G consecutive new tokens of one sequence times the
+ * G = num_heads / num_kv_heads query heads of one KV head -- and reads the
+ * context once for all of them, up to its last token; waves serving
+ * neighbouring tokens of one sequence and KV head run on one XCD, so their
+ * reads meet in its L2.  There is no split over the context and no workspace.
+ *   Source: as paged_attention_varlen (causal attention of a sequence's new
+ *   tokens over its paged context).
+ *
+ * Arguments as in paged_attention_varlen, except:
+ * max_q_len      an upper bound of the new tokens of any sequence (after the
+ *                clamp into [0, L_s]); tokens of a sequence at index
+ *                >= max_q_len are not computed and their rows not written.
+ * (no partition_size, no workspace)
+ * Supported: G in {1, 2, 4, 8, 16}, head_dim 64 or 128, the dtype pairs of
+ * paged_attention_decode; otherwise PKV_ERR_UNSUPPORTED (use
+ * paged_attention_varlen).  Rows no sequence claims, or outside
+ * [0, num_q_rows), are not written.
+ * Errors: as paged_attention_varlen; PKV_ERR_INVALID_ARG also for
+ * max_q_len < 0.  num_seqs, num_q_rows or max_q_len == 0 is a no-op.
+ */
+int paged_attention_prefill(void* out,
+                            const void* q, int q_dtype, const int32_t* cu_seqlens_q, int32_t num_q_rows,
+                            int32_t max_q_len,
+                            const void* k_cache, const void* v_cache, int cache_dtype,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float scale, float k_scale, float v_scale,
+                            void* stream);
+
+/*
  * pkv_check_inputs -- count the contents of the index arrays that the kernels
  * treat as invalid.  The write and decode stay memory-safe for any contents
  * (an out-of-range table entry is an empty block, a length is clamped into

@@ -25,7 +25,7 @@ import ctypes
 import os
 
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
-           "BlockManager", "paged_kv_copy_blocks",
+           "BlockManager", "paged_kv_copy_blocks", "paged_attention_varlen", "paged_attention_prefill",
            "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
 BLOCK_SIZE = 16
@@ -73,6 +73,9 @@ def _load():
     lib.paged_attention_varlen.argtypes = [p, p, ctypes.c_int, p, i32, p, p, ctypes.c_int, p, i32, p,
                                            i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
     lib.paged_attention_varlen.restype = ctypes.c_int
+    lib.paged_attention_prefill.argtypes = [p, p, ctypes.c_int, p, i32, i32, p, p, ctypes.c_int, p, i32, p,
+                                            i32, i32, i32, i32, i32, i32, f32, f32, f32, p]
+    lib.paged_attention_prefill.restype = ctypes.c_int
     lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
     lib.pkv_check_inputs.restype = ctypes.c_int
     i64 = ctypes.c_int64
@@ -307,6 +310,27 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
                                     B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), float(k_scale), float(v_scale),
                                     int(partition_size), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "paged_attention_varlen")
+
+
+def paged_attention_prefill(out, q, cu_seqlens_q, k_cache, v_cache, block_table, context_lens, scale: float,
+                            max_q_len: int, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """The result of paged_attention_varlen, computed in 64-column tiles per wave (long chunks of new
+    tokens).  max_q_len bounds any sequence's new-token count; no workspace."""
+    lib = _load()
+    T, Hq, D = q.shape
+    NB, Hkv, Dc = _pools(k_cache, v_cache)
+    if out.shape != q.shape or Dc != D:
+        raise ValueError("shape mismatch")
+    B = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.shape != (B + 1,):
+        raise ValueError("block_table must be [B, max_blocks] and cu_seqlens_q [B + 1]")
+    MB = block_table.shape[1]
+    st = lib.paged_attention_prefill(_dev(out, "out"), _dev(q, "q"), _dtype_code(q), _dev(cu_seqlens_q, "cu_seqlens_q"),
+                                     T, int(max_q_len), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                     _dtype_code(k_cache), _dev(block_table, "block_table"), MB,
+                                     _dev(context_lens, "context_lens"), B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale),
+                                     float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "paged_attention_prefill")
 
 
 def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_mapping=None, stream=None):

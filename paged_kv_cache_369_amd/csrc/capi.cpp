@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -269,6 +269,68 @@ int paged_attention_varlen(void* out,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
                        partition_size, nullptr, nullptr, false, cu_seqlens_q, num_q_rows, true, workspace,
                        workspace_bytes, stream);
+}
+
+int paged_attention_prefill(void* out,
+                            const void* q, int q_dtype, const int32_t* cu_seqlens_q, int32_t num_q_rows,
+                            int32_t max_q_len,
+                            const void* k_cache, const void* v_cache, int cache_dtype,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float scale, float k_scale, float v_scale,
+                            void* stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks < 0 || max_blocks_per_seq < 0 || num_q_rows < 0 || max_q_len < 0)
+        return PKV_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+    if (!known_dtype(q_dtype) || !known_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+    if (block_size != pkv::kBlockTokens || (head_dim != 64 && head_dim != 128)) return PKV_ERR_UNSUPPORTED;
+    const bool pair_ok = (q_dtype == PKV_DTYPE_F32 && cache_dtype == PKV_DTYPE_F32) ||
+                         (q_dtype == PKV_DTYPE_BF16 && cache_dtype == PKV_DTYPE_BF16) ||
+                         (q_dtype == PKV_DTYPE_BF16 && cache_dtype == PKV_DTYPE_FP8_E4M3);
+    if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == PKV_DTYPE_FP8_E4M3;
+    if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return PKV_ERR_INVALID_ARG;
+    if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
+    const int group = num_heads / num_kv_heads;
+    if (group > 16 || pkv::kPrefillWaveCols % group != 0) return PKV_ERR_UNSUPPORTED;
+    if (int64_t(num_q_rows) * num_heads * head_dim >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+    const int tpw = pkv::kPrefillWaveCols / group;
+    const int64_t items = int64_t(num_seqs) * num_kv_heads * ((int64_t(max_q_len) + tpw - 1) / tpw);
+    if (items + 8 >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_q_rows == 0 || max_q_len == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !context_lens || !cu_seqlens_q || (!block_table && max_blocks_per_seq > 0))
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(cu_seqlens_q, 4))
+        return PKV_ERR_ALIGNMENT;
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.group = group;
+    const float log2e = 1.4426950408889634f;
+    a.score_scale = scale * (fp8 ? k_scale : 1.0f) * log2e;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    a.cu_q = cu_seqlens_q;
+    a.num_q_rows = num_q_rows;
+    a.max_q = max_q_len;
+    const hipError_t e =
+        pkv::launch_prefill(cache_dtype, head_dim, a, int(items), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 int paged_kv_copy_blocks(void* k_cache, void* v_cache, int cache_dtype, int32_t num_kv_heads, int32_t head_dim,

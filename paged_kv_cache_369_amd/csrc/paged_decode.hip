@@ -1263,6 +1263,117 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- tiled prefill: many new query tokens of one sequence against its context ----
+//
+// The same attention as the several-queries mode (a new token at position p
+// sees positions 0..p of its sequence), in a shape for long chunks of new
+// tokens: one wave owns kPrefillCols query columns -- kPrefillCols / G
+// consecutive new tokens times the G query heads of one KV head -- as four
+// matrix-core column tiles, and walks the context once for all of them.
+// Each K/V tile read feeds 4x the matrix steps of a decode run, and waves
+// holding neighbouring token tiles of one (sequence, KV head) are placed on
+// one XCD so their context reads meet in its L2.  No split over the
+// context: a wave keeps the softmax states of its 64 columns to the end.
+constexpr int kPrefillCols = kPrefillWaveCols;
+constexpr int kPrefillTiles = kPrefillCols / 16;
+
+template <int KV, int D, int P>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void paged_prefill_kernel(DecodeArgs a) {
+    using GE = Geo<KV, D>;
+    using T = Tile<KV, D>;
+    constexpr int QT = (KV == kF32) ? kF32 : kBF16;
+    constexpr int NVC = GE::NVC;
+    constexpr int CT = kPrefillTiles;
+    const int lane = lane_id(), col = lane & 15;
+    const int G = a.group;
+    const int tpw = kPrefillCols / G;  // new tokens per wave
+    // work item (sequence, KV head, token tile), token tile fastest; the
+    // items of one XCD (workgroup w runs on XCD w mod 8) are consecutive
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const uint32_t ntt = uint32_t((a.max_q + tpw - 1) / tpw);
+    const int tt = int(item % ntt);
+    const uint32_t rest = item / ntt;
+    const int kvh = int(rest % uint32_t(a.num_kv_heads));
+    const int s = int(rest / uint32_t(a.num_kv_heads));
+    if (s >= a.num_seqs) return;
+    const int L = clamped_len(a, s);
+    const int q0 = a.cu_q[s];
+    const int nq = min(max(a.cu_q[s + 1] - q0, 0), L);
+    const int t0 = tt * tpw;
+    if (t0 >= nq) return;
+    const int tend = min(t0 + tpw, nq);
+    const int ctx = L - nq + tend;  // positions the wave's last token sees
+    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
+
+    // columns: column tile c, lane column col -> token t0 + k / G, head kvh * G + k % G (k = 16 c + col)
+    QOp<KV> qop[CT][GE::NQ];
+    int vis[CT];      // positions this lane's column sees
+    int64_t row[CT];  // its output row (query row * num_heads + head)
+    bool hv[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const int k = 16 * c + col;
+        const int tok = t0 + k / G;
+        const bool ok = tok < tend && q0 >= 0 && int64_t(q0) + tok < int64_t(a.num_q_rows);
+        hv[c] = ok;
+        row[c] = (ok ? int64_t(q0) + tok : 0) * a.num_heads + kvh * G + k % G;
+        vis[c] = ok ? L - nq + tok + 1 : ctx;
+        load_q<KV, D>(a, row[c], ok, qop[c]);
+    }
+    Run<NVC> rs[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) run_reset(rs[c]);
+
+    // block ids of the next 64 blocks to load (lane l: block jb + l), and of the 64 after them
+    const int32_t* bt = a.block_table + int64_t(s) * a.max_blocks;
+    int jb = 0;
+    int ids = lane < nblk ? bt[lane] : -1;
+    int idsn = 64 + lane < nblk ? bt[64 + lane] : -1;
+    auto issue = [&](T& tb, int& nv, int j) {
+        if (j - jb >= 64) {  // positions only grow: move to the next window
+            jb += 64;
+            ids = idsn;
+            idsn = jb + 64 + lane < nblk ? bt[jb + 64 + lane] : -1;
+        }
+        const int id = j < nblk ? __builtin_amdgcn_readlane(ids, j - jb) : -1;
+        const bool ok = id >= 0 && id < a.num_blocks;
+        nv = ok ? min(kBlockTokens, L - j * kBlockTokens) : 0;
+        load_tile<KV, D>(a, ok ? kvh : 0, ok ? id : 0, tb);
+    };
+    T buf[P];
+    int nvb[P];
+#pragma unroll
+    for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], k);
+    for (int j = 0; j < nblk; j += P) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int jj = j + k;
+            if (jj < nblk) {
+                issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], jj + P - 1);
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+                    consume_tile<KV, D, true>(a, buf[k], nvb[k], vis[c] - jj * kBlockTokens, qop[c], rs[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        State<NVC> st;
+        run_close(rs[c], st);
+        state_output<QT, D>(a, row[c], st, hv[c]);
+    }
+}
+
+template <int KV, int D>
+hipError_t launch_prefill_t(const DecodeArgs& a, int items, hipStream_t stream) {
+    // one wave per SIMD: one tile deeper than the decode, except fp32 at head_dim 128 (tiles of 16 KiB)
+    constexpr int P = (KV == kF32 && D == 128) ? 2 : Depth<KV, D>::P + 1;
+    const int grid = (items + 7) / 8 * 8;
+    hipLaunchKernelGGL((paged_prefill_kernel<KV, D, P>), dim3(grid), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 template <int M>
@@ -1273,6 +1384,17 @@ hipError_t launch_c(int cache_dtype, int head_dim, const DecodeArgs& a, hipStrea
     if (cache_dtype == kBF16 && head_dim == 128) return launch_t<kBF16, 128, M>(a, stream);
     if (cache_dtype == kFP8 && head_dim == 64) return launch_t<kFP8, 64, M>(a, stream);
     if (cache_dtype == kFP8 && head_dim == 128) return launch_t<kFP8, 128, M>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(int cache_dtype, int head_dim, const DecodeArgs& a, int items, hipStream_t stream) {
+    if (items == 0) return hipSuccess;
+    if (cache_dtype == kF32 && head_dim == 64) return launch_prefill_t<kF32, 64>(a, items, stream);
+    if (cache_dtype == kF32 && head_dim == 128) return launch_prefill_t<kF32, 128>(a, items, stream);
+    if (cache_dtype == kBF16 && head_dim == 64) return launch_prefill_t<kBF16, 64>(a, items, stream);
+    if (cache_dtype == kBF16 && head_dim == 128) return launch_prefill_t<kBF16, 128>(a, items, stream);
+    if (cache_dtype == kFP8 && head_dim == 64) return launch_prefill_t<kFP8, 64>(a, items, stream);
+    if (cache_dtype == kFP8 && head_dim == 128) return launch_prefill_t<kFP8, 128>(a, items, stream);
     return hipErrorInvalidValue;
 }
 

@@ -113,6 +113,8 @@ struct DecodeArgs {
     // several new query tokens per sequence only (null / 0 otherwise)
     const int32_t* cu_q;           // [num_seqs + 1] first query row of each sequence
     int32_t num_q_rows;            // rows of q and out
+    // tiled prefill only
+    int32_t max_q;                 // new tokens of the longest sequence (tokens past it are not computed)
 };
 
 // What the decode kernel computes: one query token per sequence, the same
@@ -126,6 +128,12 @@ inline int64_t align_floats(int64_t n) { return (n + 63) / 64 * 64; }
 inline int64_t state_row_floats(int head_dim) { return int64_t(head_dim) + 4; }
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+
+// Query columns of one prefill wave: kPrefillWaveCols / G new tokens times the
+// G query heads of one KV head (G must divide it and be at most 16).
+constexpr int kPrefillWaveCols = 64;
+// Tiled prefill over `items` = num_seqs * num_kv_heads * ceil(max_q * G / 64) waves.
+hipError_t launch_prefill(int cache_dtype, int head_dim, const DecodeArgs& a, int items, hipStream_t stream);
 
 struct CheckArgs {
     const int32_t* block_table;

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 7
+    assert lib.pkv_abi_version() == 8
     for st in range(7):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -204,3 +204,31 @@ def test_varlen_validation_and_workspace(lib):
     assert _var(lib, wsb=vws(4, 32, 8, 128, 64, 16, 0) - 1) == WORKSPACE
     assert _var(lib, T=0) == OK
     assert _var(lib, B=0) == OK
+
+
+def _pre(lib, **kw):
+    a = dict(out=A, q=A, qd=1, cu=A, T=512, mq=512, kc=A, vc=A, cd=1, bt=A, MB=64, cl=A, B=4, H=32, Hkv=8, D=128,
+             bs=16, NB=300, scale=0.088, ks=1.0, vs=1.0)
+    a.update(kw)
+    return lib.paged_attention_prefill(a["out"], a["q"], a["qd"], a["cu"], a["T"], a["mq"], a["kc"], a["vc"], a["cd"],
+                                       a["bt"], a["MB"], a["cl"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                       a["scale"], a["ks"], a["vs"], None)
+
+
+def test_prefill_validation(lib):
+    assert _pre(lib, cu=0) == INVALID
+    assert _pre(lib, T=-1) == INVALID
+    assert _pre(lib, mq=-1) == INVALID
+    assert _pre(lib, H=30, Hkv=8) == INVALID                     # heads not a multiple of KV heads
+    assert _pre(lib, cu=A + 2) == ALIGN
+    assert _pre(lib, out=A + 8) == ALIGN
+    assert _pre(lib, qd=0, cd=1) == UNSUPPORTED
+    assert _pre(lib, H=24, Hkv=8) == UNSUPPORTED                 # group 3 does not divide the 64 columns of a wave
+    assert _pre(lib, H=64, Hkv=2) == UNSUPPORTED                 # group 32 > 16
+    assert _pre(lib, D=96) == UNSUPPORTED
+    assert _pre(lib, bs=32) == UNSUPPORTED
+    assert _pre(lib, T=1 << 20, H=64, D=128) == UNSUPPORTED      # rows * heads * head_dim reach 2^31
+    assert _pre(lib, cd=2, ks=0.0) == INVALID                     # fp8 pool needs positive scales
+    assert _pre(lib, T=0) == OK
+    assert _pre(lib, B=0) == OK
+    assert _pre(lib, mq=0) == OK
