@@ -140,9 +140,9 @@ def prefill_flops(w) -> int:
 
 
 def prefill_read_bytes(w) -> int:
-    """KV bytes the tiled prefill reads from the pools at most: each wave (64 / G new tokens of one sequence and
+    """KV bytes the tiled prefill reads from the pools at most: each wave (32 / G new tokens of one sequence and
     KV head) reads the context up to its last token; waves that share a context on one XCD meet in its L2."""
-    tpw = 64 // (w.num_heads // w.num_kv_heads)
+    tpw = 32 // (w.num_heads // w.num_kv_heads)
     tokens = 0
     for s, L in enumerate(w.context_lens.tolist()):
         n = int(w.cu_q[s + 1] - w.cu_q[s])
@@ -499,7 +499,7 @@ def main() -> int:
     ap.add_argument("--cascade", action="store_true",
                     help="decode with paged_attention_decode_cascade using the workload's sharing arrays")
     ap.add_argument("--prefill", action="store_true",
-                    help="several-token workloads: time paged_attention_prefill (64-column tiles per wave) "
+                    help="several-token workloads: time paged_attention_prefill (32 query columns per wave) "
                          "instead of paged_attention_varlen")
     ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
                     help="read (or overwrite) 512 MB before every step, outside the timed brackets, so the step's "

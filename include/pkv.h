@@ -303,8 +303,8 @@ int paged_attention_varlen(void* out,
 
 /*
  * paged_attention_prefill -- the same result as paged_attention_varlen, in a
- * shape for long chunks of new tokens (chunked prefill).  One wave serves 64
- * query columns -- 64 / G consecutive new tokens of one sequence times the
+ * shape for long chunks of new tokens (chunked prefill).  One wave serves 32
+ * query columns -- 32 / G consecutive new tokens of one sequence times the
  * G = num_heads / num_kv_heads query heads of one KV head -- and reads the
  * context once for all of them, up to its last token; waves serving
  * neighbouring tokens of one sequence and KV head run on one XCD, so their

@@ -314,7 +314,7 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
 
 def paged_attention_prefill(out, q, cu_seqlens_q, k_cache, v_cache, block_table, context_lens, scale: float,
                             max_q_len: int, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
-    """The result of paged_attention_varlen, computed in 64-column tiles per wave (long chunks of new
+    """The result of paged_attention_varlen, computed 32 query columns per wave (long chunks of new
     tokens).  max_q_len bounds any sequence's new-token count; no workspace."""
     lib = _load()
     T, Hq, D = q.shape

@@ -1267,18 +1267,145 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 //
 // The same attention as the several-queries mode (a new token at position p
 // sees positions 0..p of its sequence), in a shape for long chunks of new
-// tokens: one wave owns kPrefillCols query columns -- kPrefillCols / G
-// consecutive new tokens times the G query heads of one KV head -- as four
+// tokens: one wave owns kPrefillCols (32) query columns -- kPrefillCols / G
+// consecutive new tokens times the G query heads of one KV head -- as two
 // matrix-core column tiles, and walks the context once for all of them.
-// Each K/V tile read feeds 4x the matrix steps of a decode run, and waves
+// Each K/V tile read feeds twice the matrix steps of a decode run, and waves
 // holding neighbouring token tiles of one (sequence, KV head) are placed on
 // one XCD so their context reads meet in its L2.  No split over the
-// context: a wave keeps the softmax states of its 64 columns to the end.
+// context: a wave keeps the softmax states of its columns to the end.
 constexpr int kPrefillCols = kPrefillWaveCols;
 constexpr int kPrefillTiles = kPrefillCols / 16;
 
+// consume_tile for CT query-column tiles at once: every score product
+// first, then each column tile's softmax update, then every value product
+// (K and V widened and V masked once for all column tiles).  Per column tile
+// the arithmetic is consume_tile's, in the same order.
+template <int KV, int D, int CT>
+__device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV, D>& t, int nv, const int (&upto)[CT],
+                                              const QOp<KV> (&qop)[CT][Geo<KV, D>::NQ],
+                                              Run<Geo<KV, D>::NVC> (&rs)[CT]) {
+    using GE = Geo<KV, D>;
+    const int g = lane_id() >> 4;
+    f32x4 sacc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV == kBF16) {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[c][u], sacc[c],
+                                                                  0, 0, 0);
+    } else if constexpr (KV == kFP8) {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u) {
+            const bf16x8 k0 = fp8x8_to_bf16x8(t.k[u].x, t.k[u].y);
+            const bf16x8 k1 = fp8x8_to_bf16x8(t.k[u].z, t.k[u].w);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[c][2 * u], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[c][2 * u + 1], sacc[c], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < GE::NKL; ++u)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[c][4 * u + 0], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[c][4 * u + 1], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[c][4 * u + 2], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[c][4 * u + 3], sacc[c], 0, 0, 0);
+            }
+    }
+    const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
+    float sv[CT][4], bm[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const int scnt = min(cnt, max(upto[c] - 4 * g, 0));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[c][r] = r < scnt ? sacc[c][r] * a.score_scale : kNegInf;
+        bm[c] = fmaxf(fmaxf(sv[c][0], sv[c][1]), fmaxf(sv[c][2], sv[c][3]));
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 16));
+#pragma unroll
+    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 32));
+    float alpha[CT], pw[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const float mn = fmaxf(rs[c].m, bm[c]);
+        const bool live = mn != kNegInf;
+        alpha[c] = live ? __builtin_amdgcn_exp2f(rs[c].m - mn) : 1.0f;
+        rs[c].m = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pw[c][r] = live ? __builtin_amdgcn_exp2f(sv[c][r] - mn) : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        if (__ballot(alpha[c] != 1.0f)) {
+#pragma unroll
+            for (int v = 0; v < GE::NVC; ++v) rs[c].acc[v] *= alpha[c];
+        }
+    }
+    if constexpr (KV == kF32) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+            rs[c].lsum = rs[c].lsum * alpha[c] + ((pw[c][0] + pw[c][1]) + (pw[c][2] + pw[c][3]));
+#pragma unroll
+        for (int v = 0; v < GE::NVC; ++v) {
+            const uint4 vv = t.v[v];
+            const float v0 = cnt > 0 ? __uint_as_float(vv.x) : 0.0f;
+            const float v1 = cnt > 1 ? __uint_as_float(vv.y) : 0.0f;
+            const float v2 = cnt > 2 ? __uint_as_float(vv.z) : 0.0f;
+            const float v3 = cnt > 3 ? __uint_as_float(vv.w) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, pw[c][0], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, pw[c][1], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, pw[c][2], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, pw[c][3], rs[c].acc[v], 0, 0, 0);
+            }
+        }
+    } else {
+        i16x4 pb[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const uint32_t p01 = pack_bf16(pw[c][0], pw[c][1]);
+            const uint32_t p23 = pack_bf16(pw[c][2], pw[c][3]);
+            rs[c].lsum = rs[c].lsum * alpha[c] + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                                                  (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+            pb[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+        }
+        const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
+        const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int v = 0; v < GE::NVC; ++v) {
+            uint2 vv;
+            if constexpr (KV == kBF16) {
+                vv = t.v[v];
+            } else {
+                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[v]), fp8x2_to_bf16x2<true>(t.v[v]));
+            }
+            vv.x &= mlo;
+            vv.y &= mhi;
+            const i16x4 va = __builtin_bit_cast(i16x4, vv);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[c], rs[c].acc[v], 0, 0, 0);
+        }
+    }
+}
+
+// Two waves per SIMD (one for fp32 pools of head_dim 128, whose tiles and
+// query operands are twice as large): the matrix steps of one wave overlap the
+// softmax of the other.
+template <int KV, int D>
+constexpr int kPrefillWaves = (KV == kF32 && D == 128) ? 1 : 2;
+
 template <int KV, int D, int P>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void paged_prefill_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWaves<KV, D>))) void paged_prefill_kernel(DecodeArgs a) {
     using GE = Geo<KV, D>;
     using T = Tile<KV, D>;
     constexpr int QT = (KV == kF32) ? kF32 : kBF16;
@@ -1351,9 +1478,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void pa
             const int jj = j + k;
             if (jj < nblk) {
                 issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], jj + P - 1);
+                int upto[CT];
 #pragma unroll
-                for (int c = 0; c < CT; ++c)
-                    consume_tile<KV, D, true>(a, buf[k], nvb[k], vis[c] - jj * kBlockTokens, qop[c], rs[c]);
+                for (int c = 0; c < CT; ++c) upto[c] = vis[c] - jj * kBlockTokens;
+                consume_tiles<KV, D, CT>(a, buf[k], nvb[k], upto, qop, rs);
             }
         }
     }
@@ -1367,8 +1495,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void pa
 
 template <int KV, int D>
 hipError_t launch_prefill_t(const DecodeArgs& a, int items, hipStream_t stream) {
-    // one wave per SIMD: one tile deeper than the decode, except fp32 at head_dim 128 (tiles of 16 KiB)
-    constexpr int P = (KV == kF32 && D == 128) ? 2 : Depth<KV, D>::P + 1;
+    // three tiles in flight (two for fp32 pools of head_dim 128, tiles of 16 KiB): deeper buys nothing,
+    // the wave is bound by its matrix and softmax steps
+#ifdef PKV_PREFILL_DEPTH
+    constexpr int P = PKV_PREFILL_DEPTH;
+#else
+    constexpr int P = (KV == kF32 && D == 128) ? 2 : 3;
+#endif
     const int grid = (items + 7) / 8 * 8;
     hipLaunchKernelGGL((paged_prefill_kernel<KV, D, P>), dim3(grid), dim3(64), 0, stream, a);
     return hipGetLastError();

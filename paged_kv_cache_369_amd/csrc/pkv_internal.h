@@ -131,8 +131,11 @@ hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hip
 
 // Query columns of one prefill wave: kPrefillWaveCols / G new tokens times the
 // G query heads of one KV head (G must divide it and be at most 16).
-constexpr int kPrefillWaveCols = 64;
-// Tiled prefill over `items` = num_seqs * num_kv_heads * ceil(max_q * G / 64) waves.
+#ifndef PKV_PREFILL_COLS
+#define PKV_PREFILL_COLS 32
+#endif
+constexpr int kPrefillWaveCols = PKV_PREFILL_COLS;
+// Tiled prefill over `items` = num_seqs * num_kv_heads * ceil(max_q * G / kPrefillWaveCols) waves.
 hipError_t launch_prefill(int cache_dtype, int head_dim, const DecodeArgs& a, int items, hipStream_t stream);
 
 struct CheckArgs {

@@ -1,7 +1,7 @@
 """GPU parity of paged_attention_prefill (tiled chunked prefill) against the oracle's varlen attention.
 
 Same result and tolerances as paged_attention_varlen (1e-5 fp32, 2e-2 bf16, 6e-2 fp8 pools): every new
-token of a sequence attends causally over its paged context.  Cases span several 64-column waves per
+token of a sequence attends causally over its paged context.  Cases span several 32-column waves per
 sequence, token tiles that end mid-chunk, chunks longer than the context's first block, every supported
 GQA group, both head sizes and all three pool types; plus unclaimed rows and a max_q_len below a
 sequence's count.
@@ -37,11 +37,11 @@ def _prefill(w, kp, vp, max_q=None, cu=None, out=None):
 
 
 @pytest.mark.parametrize("hq,hkv,d,cache", [
-    (32, 8, 128, "bf16"),   # GQA 4: 16 tokens per wave
-    (8, 8, 128, "bf16"),    # one head per KV head: 64 tokens per wave
-    (64, 8, 128, "fp8"),    # GQA 8: 8 tokens per wave
+    (32, 8, 128, "bf16"),   # GQA 4: 8 tokens per wave
+    (8, 8, 128, "bf16"),    # one head per KV head: 32 tokens per wave
+    (64, 8, 128, "fp8"),    # GQA 8: 4 tokens per wave
     (16, 8, 64, "f32"),     # GQA 2
-    (32, 2, 64, "bf16"),    # GQA 16: 4 tokens per wave
+    (32, 2, 64, "bf16"),    # GQA 16: 2 tokens per wave
     (32, 8, 128, "f32"),
 ])
 @pytest.mark.parametrize("pat", range(len(PATTERNS)))
