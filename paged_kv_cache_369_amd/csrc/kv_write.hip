@@ -115,7 +115,10 @@ __device__ __forceinline__ uint4 cache_chunk(const uint8_t* src, float scale) {
 //  4. Tokens that are not covered store their elements one by one.
 // Every element of a token with a valid slot is written exactly once, by
 // step 2 (K), 3 or 4 (V).
-constexpr int kGroup = 64;
+#ifndef PKV_WRITE_GROUP
+#define PKV_WRITE_GROUP 64
+#endif
+constexpr int kGroup = PKV_WRITE_GROUP;  // at most 64: step 3a runs in one wave
 
 template <int IN, int CT, int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict__ k_new,

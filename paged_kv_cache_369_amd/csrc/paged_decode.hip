@@ -544,93 +544,138 @@ __device__ __forceinline__ void run_close(const Run<NVC>& r, State<NVC>& st) {
     for (int c = 0; c < NVC; ++c) st.acc[c] = r.acc[c];
 }
 
-// Steps 2-4 for one block with nv valid tokens.  With CAUSAL, this lane's
-// column scores only the block's first `upto` tokens (its token's position is
-// upto - 1 relative to the block); the values stay masked by nv only.
-template <int KV, int D, bool CAUSAL>
-__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv, int upto,
-                                             const QOp<KV> (&qop)[Geo<KV, D>::NQ], Run<Geo<KV, D>::NVC>& rs) {
+// Steps 2-4 for one block with nv valid tokens, for CT query-column tiles
+// at once: every score product first, then each column tile's softmax
+// update, then every value product (K and V widened, and V masked, once for
+// all column tiles).  With CAUSAL, this lane's column of tile c scores only
+// the block's first upto[c] tokens (its token's position is upto[c] - 1
+// relative to the block); the values stay masked by nv only.
+template <int KV, int D, int CT, bool CAUSAL>
+__device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV, D>& t, int nv, const int (&upto)[CT],
+                                              const QOp<KV> (&qop)[CT][Geo<KV, D>::NQ],
+                                              Run<Geo<KV, D>::NVC> (&rs)[CT]) {
     using GE = Geo<KV, D>;
     const int g = lane_id() >> 4;
-    // 2. scores: sacc[r] = S^T[token 4g + r][head col]
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sacc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (KV == kBF16) {
 #pragma unroll
         for (int u = 0; u < GE::NKL; ++u)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[u], sacc, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[c][u], sacc[c],
+                                                                  0, 0, 0);
     } else if constexpr (KV == kFP8) {
 #pragma unroll
         for (int u = 0; u < GE::NKL; ++u) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].x, t.k[u].y), qop[2 * u], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t.k[u].z, t.k[u].w), qop[2 * u + 1], sacc, 0, 0, 0);
+            const bf16x8 k0 = fp8x8_to_bf16x8(t.k[u].x, t.k[u].y);
+            const bf16x8 k1 = fp8x8_to_bf16x8(t.k[u].z, t.k[u].w);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[c][2 * u], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[c][2 * u + 1], sacc[c], 0, 0, 0);
+            }
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < GE::NKL; ++u) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[4 * u + 0], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[4 * u + 1], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[4 * u + 2], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[4 * u + 3], sacc, 0, 0, 0);
+        for (int u = 0; u < GE::NKL; ++u)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[c][4 * u + 0], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[c][4 * u + 1], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[c][4 * u + 2], sacc[c], 0, 0, 0);
+                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[c][4 * u + 3], sacc[c], 0, 0, 0);
+            }
+    }
+    const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
+    float sv[CT][4], bm[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const int scnt = CAUSAL ? min(cnt, max(upto[c] - 4 * g, 0)) : cnt;  // ... that this column may see
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[c][r] = r < scnt ? sacc[c][r] * a.score_scale : kNegInf;
+        bm[c] = fmaxf(fmaxf(sv[c][0], sv[c][1]), fmaxf(sv[c][2], sv[c][3]));
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 16));
+#pragma unroll
+    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 32));
+    float alpha[CT], pw[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const float mn = fmaxf(rs[c].m, bm[c]);
+        const bool live = mn != kNegInf;
+        alpha[c] = live ? __builtin_amdgcn_exp2f(rs[c].m - mn) : 1.0f;
+        rs[c].m = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pw[c][r] = live ? __builtin_amdgcn_exp2f(sv[c][r] - mn) : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        if (__ballot(alpha[c] != 1.0f)) {
+#pragma unroll
+            for (int v = 0; v < GE::NVC; ++v) rs[c].acc[v] *= alpha[c];
         }
     }
-    // 3. online softmax for head `col`
-    const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
-    const int scnt = CAUSAL ? min(cnt, max(upto - 4 * g, 0)) : cnt;  // ... that this column may see
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = r < scnt ? sacc[r] * a.score_scale : kNegInf;
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(rs.m, bm);
-    const bool live = mn != kNegInf;
-    const float alpha = live ? __builtin_amdgcn_exp2f(rs.m - mn) : 1.0f;
-    rs.m = mn;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = live ? __builtin_amdgcn_exp2f(sv[r] - mn) : 0.0f;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int c = 0; c < GE::NVC; ++c) rs.acc[c] *= alpha;
-    }
-    // 4. O^T += V^T P^T
     if constexpr (KV == kF32) {
-        rs.lsum = rs.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
-        for (int c = 0; c < GE::NVC; ++c) {
-            const uint4 vv = t.v[c];
+        for (int c = 0; c < CT; ++c)
+            rs[c].lsum = rs[c].lsum * alpha[c] + ((pw[c][0] + pw[c][1]) + (pw[c][2] + pw[c][3]));
+#pragma unroll
+        for (int v = 0; v < GE::NVC; ++v) {
+            const uint4 vv = t.v[v];
             const float v0 = cnt > 0 ? __uint_as_float(vv.x) : 0.0f;
             const float v1 = cnt > 1 ? __uint_as_float(vv.y) : 0.0f;
             const float v2 = cnt > 2 ? __uint_as_float(vv.z) : 0.0f;
             const float v3 = cnt > 3 ? __uint_as_float(vv.w) : 0.0f;
-            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, p[0], rs.acc[c], 0, 0, 0);
-            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, p[1], rs.acc[c], 0, 0, 0);
-            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, p[2], rs.acc[c], 0, 0, 0);
-            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, p[3], rs.acc[c], 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, pw[c][0], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, pw[c][1], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, pw[c][2], rs[c].acc[v], 0, 0, 0);
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, pw[c][3], rs[c].acc[v], 0, 0, 0);
+            }
         }
     } else {
-        const uint32_t p01 = pack_bf16(p[0], p[1]);
-        const uint32_t p23 = pack_bf16(p[2], p[3]);
-        // the normaliser sums the rounded weights the products use
-        rs.lsum = rs.lsum * alpha + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
-        const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
-        // keep-masks for this lane's four tokens (16 bits per bf16 token)
+        i16x4 pb[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const uint32_t p01 = pack_bf16(pw[c][0], pw[c][1]);
+            const uint32_t p23 = pack_bf16(pw[c][2], pw[c][3]);
+            rs[c].lsum = rs[c].lsum * alpha[c] + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                                                  (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+            pb[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+        }
         const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
         const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
-        for (int c = 0; c < GE::NVC; ++c) {
+        for (int v = 0; v < GE::NVC; ++v) {
             uint2 vv;
             if constexpr (KV == kBF16) {
-                vv = t.v[c];
+                vv = t.v[v];
             } else {
-                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[c]), fp8x2_to_bf16x2<true>(t.v[c]));
+                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[v]), fp8x2_to_bf16x2<true>(t.v[v]));
             }
             vv.x &= mlo;
             vv.y &= mhi;
-            rs.acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vv), pb, rs.acc[c], 0, 0, 0);
+            const i16x4 va = __builtin_bit_cast(i16x4, vv);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[c], rs[c].acc[v], 0, 0, 0);
         }
     }
+}
+
+// Two waves per SIMD (one for fp32 pools of head_dim 128, whose tiles and
+// query operands are twice as large): the matrix steps of one wave overlap the
+// softmax of the other.
+template <int KV, int D, bool CAUSAL>
+__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv, int upto,
+                                             const QOp<KV> (&qop)[Geo<KV, D>::NQ], Run<Geo<KV, D>::NVC>& rs) {
+    const int up[1] = {upto};
+    consume_tiles<KV, D, 1, CAUSAL>(a, t, nv, up, reinterpret_cast<const QOp<KV>(&)[1][Geo<KV, D>::NQ]>(qop),
+                                    reinterpret_cast<Run<Geo<KV, D>::NVC>(&)[1]>(rs));
 }
 
 // Stretch geometry, identical in every wave.  Stretch t of nw covers units
@@ -1277,130 +1322,6 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 constexpr int kPrefillCols = kPrefillWaveCols;
 constexpr int kPrefillTiles = kPrefillCols / 16;
 
-// consume_tile for CT query-column tiles at once: every score product
-// first, then each column tile's softmax update, then every value product
-// (K and V widened and V masked once for all column tiles).  Per column tile
-// the arithmetic is consume_tile's, in the same order.
-template <int KV, int D, int CT>
-__device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV, D>& t, int nv, const int (&upto)[CT],
-                                              const QOp<KV> (&qop)[CT][Geo<KV, D>::NQ],
-                                              Run<Geo<KV, D>::NVC> (&rs)[CT]) {
-    using GE = Geo<KV, D>;
-    const int g = lane_id() >> 4;
-    f32x4 sacc[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KV == kBF16) {
-#pragma unroll
-        for (int u = 0; u < GE::NKL; ++u)
-#pragma unroll
-            for (int c = 0; c < CT; ++c)
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u]), qop[c][u], sacc[c],
-                                                                  0, 0, 0);
-    } else if constexpr (KV == kFP8) {
-#pragma unroll
-        for (int u = 0; u < GE::NKL; ++u) {
-            const bf16x8 k0 = fp8x8_to_bf16x8(t.k[u].x, t.k[u].y);
-            const bf16x8 k1 = fp8x8_to_bf16x8(t.k[u].z, t.k[u].w);
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[c][2 * u], sacc[c], 0, 0, 0);
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[c][2 * u + 1], sacc[c], 0, 0, 0);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < GE::NKL; ++u)
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].x), qop[c][4 * u + 0], sacc[c], 0, 0, 0);
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].y), qop[c][4 * u + 1], sacc[c], 0, 0, 0);
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].z), qop[c][4 * u + 2], sacc[c], 0, 0, 0);
-                sacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k[u].w), qop[c][4 * u + 3], sacc[c], 0, 0, 0);
-            }
-    }
-    const int cnt = min(max(nv - 4 * g, 0), 4);  // valid tokens among this lane's four
-    float sv[CT][4], bm[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const int scnt = min(cnt, max(upto[c] - 4 * g, 0));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[c][r] = r < scnt ? sacc[c][r] * a.score_scale : kNegInf;
-        bm[c] = fmaxf(fmaxf(sv[c][0], sv[c][1]), fmaxf(sv[c][2], sv[c][3]));
-    }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 16));
-#pragma unroll
-    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 32));
-    float alpha[CT], pw[CT][4];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const float mn = fmaxf(rs[c].m, bm[c]);
-        const bool live = mn != kNegInf;
-        alpha[c] = live ? __builtin_amdgcn_exp2f(rs[c].m - mn) : 1.0f;
-        rs[c].m = mn;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pw[c][r] = live ? __builtin_amdgcn_exp2f(sv[c][r] - mn) : 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        if (__ballot(alpha[c] != 1.0f)) {
-#pragma unroll
-            for (int v = 0; v < GE::NVC; ++v) rs[c].acc[v] *= alpha[c];
-        }
-    }
-    if constexpr (KV == kF32) {
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-            rs[c].lsum = rs[c].lsum * alpha[c] + ((pw[c][0] + pw[c][1]) + (pw[c][2] + pw[c][3]));
-#pragma unroll
-        for (int v = 0; v < GE::NVC; ++v) {
-            const uint4 vv = t.v[v];
-            const float v0 = cnt > 0 ? __uint_as_float(vv.x) : 0.0f;
-            const float v1 = cnt > 1 ? __uint_as_float(vv.y) : 0.0f;
-            const float v2 = cnt > 2 ? __uint_as_float(vv.z) : 0.0f;
-            const float v3 = cnt > 3 ? __uint_as_float(vv.w) : 0.0f;
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, pw[c][0], rs[c].acc[v], 0, 0, 0);
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, pw[c][1], rs[c].acc[v], 0, 0, 0);
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, pw[c][2], rs[c].acc[v], 0, 0, 0);
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, pw[c][3], rs[c].acc[v], 0, 0, 0);
-            }
-        }
-    } else {
-        i16x4 pb[CT];
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            const uint32_t p01 = pack_bf16(pw[c][0], pw[c][1]);
-            const uint32_t p23 = pack_bf16(pw[c][2], pw[c][3]);
-            rs[c].lsum = rs[c].lsum * alpha[c] + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                                                  (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
-            pb[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
-        }
-        const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
-        const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-        for (int v = 0; v < GE::NVC; ++v) {
-            uint2 vv;
-            if constexpr (KV == kBF16) {
-                vv = t.v[v];
-            } else {
-                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[v]), fp8x2_to_bf16x2<true>(t.v[v]));
-            }
-            vv.x &= mlo;
-            vv.y &= mhi;
-            const i16x4 va = __builtin_bit_cast(i16x4, vv);
-#pragma unroll
-            for (int c = 0; c < CT; ++c)
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[c], rs[c].acc[v], 0, 0, 0);
-        }
-    }
-}
-
-// Two waves per SIMD (one for fp32 pools of head_dim 128, whose tiles and
-// query operands are twice as large): the matrix steps of one wave overlap the
-// softmax of the other.
 template <int KV, int D>
 constexpr int kPrefillWaves = (KV == kF32 && D == 128) ? 1 : 2;
 
@@ -1481,7 +1402,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
                 int upto[CT];
 #pragma unroll
                 for (int c = 0; c < CT; ++c) upto[c] = vis[c] - jj * kBlockTokens;
-                consume_tiles<KV, D, CT>(a, buf[k], nvb[k], upto, qop, rs);
+                consume_tiles<KV, D, CT, true>(a, buf[k], nvb[k], upto, qop, rs);
             }
         }
     }
