@@ -78,6 +78,9 @@ def decode_source_digest() -> str:
 
 
 def traffic_file(workload: str, directory: str = PROFILES) -> str:
+    """profiles/paged_decode_<workload>_hbm_traffic.json, or paged_prefill_<workload> for a '-prefill' key."""
+    if workload.endswith("-prefill"):
+        return os.path.join(directory, f"paged_prefill_{workload[:-len('-prefill')]}_hbm_traffic.json")
     return os.path.join(directory, f"paged_decode_{workload}_hbm_traffic.json")
 
 
@@ -149,6 +152,11 @@ def prefill_read_bytes(w) -> int:
         for t in range(0, n, tpw):
             tokens += L - n + min(t + tpw, n)
     return tokens * w.num_kv_heads * w.head_dim * 2 * w.kv_elt_bytes()
+
+
+def kernel_key(args) -> str:
+    """The kernel a counter summary covers: the prefill's for --prefill, else the decode's."""
+    return "paged_prefill_kernel" if args.prefill else "paged_decode_kernel"
 
 
 def profile_key(args) -> str:
@@ -349,14 +357,14 @@ def summarize_counters(args) -> int:
     vals = {}
     for d in args.counter_dirs:
         for r in _csv_rows(d, "counter_collection.csv"):
-            if "paged_decode_kernel" not in r["Kernel_Name"]:
+            if kernel_key(args) not in r["Kernel_Name"]:
                 continue
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if not vals:
-        raise SystemExit("no paged_decode_kernel rows in the counter runs")
+        raise SystemExit(f"no {kernel_key(args)} rows in the counter runs")
     mean = {k: sum(v) / len(v) for k, v in vals.items()}
     from paged_kv_cache_369_amd import workloads as W
-    lines = [f"# SQ counters of `paged_decode_kernel`, workload `{profile_key(args)}`", "",
+    lines = [f"# SQ counters of `{kernel_key(args)}`, workload `{profile_key(args)}`", "",
              WORKLOAD_DESC[args.workload] + (CASCADE_NOTE if args.cascade else ""), "",
              "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in args.commands]
@@ -402,14 +410,15 @@ def summarize_traffic(args) -> int:
     fetch = _per_kernel(args.dec_fetch, "FETCH_SIZE")
     write = _per_kernel(args.dec_write, "WRITE_SIZE")
     kernels = {}
-    for key in ("paged_decode_kernel",):
+    for key in (kernel_key(args),):
         f_kib, w_kib = _pick(fetch, key), _pick(write, key)
         kernels[key] = {"fetch_kib": f_kib, "write_kib": w_kib,
                         "fetch_bytes": f_kib * 1024 * fscale, "write_bytes": w_kib * 1024 * wscale}
     total = sum(k["fetch_bytes"] + k["write_bytes"] for k in kernels.values())
     from paged_kv_cache_369_amd import workloads as W
     w = W.make(args.workload)
-    kv = cascade_read_bytes(w) if args.cascade else w.kv_bytes()
+    kv = (cascade_read_bytes(w) if args.cascade else prefill_read_bytes(w) if args.prefill else
+          varlen_read_bytes(w) if w.cu_q is not None else w.kv_bytes())
     rec = {"workload": profile_key(args), "source_digest": decode_source_digest(),
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                                 "fetch_scale": fscale, "write_scale": wscale},
@@ -421,7 +430,7 @@ def summarize_traffic(args) -> int:
         f.write("\n")
     md = traffic_file(profile_key(args), args.out_dir).replace(".json", ".md")
     with open(md, "w") as f:
-        f.write(f"# HBM traffic of one decode call, workload `{profile_key(args)}`\n\n")
+        f.write(f"# HBM traffic of one {'prefill' if args.prefill else 'decode'} call, workload `{profile_key(args)}`\n\n")
         f.write(f"{WORKLOAD_DESC[args.workload]}{CASCADE_NOTE if args.cascade else ''}.\n\n"
                 "Commands (run from the repository root):\n\n")
         for c in args.commands:
@@ -434,8 +443,9 @@ def summarize_traffic(args) -> int:
         for key, k in kernels.items():
             f.write(f"| `{key}` | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | {k['fetch_bytes'] / 1e6:.1f} | "
                     f"{k['write_bytes'] / 1e6:.1f} |\n")
-        f.write(f"\nTotal per decode call: {total / 1e6:.1f} MB of HBM traffic against {kv / 1e6:.1f} MB of "
-                f"algorithmic KV bytes (ratio {total / kv:.4f}).  Decode source digest `{rec['source_digest']}`.\n")
+        f.write(f"\nTotal per call: {total / 1e6:.1f} MB of HBM traffic against {kv / 1e6:.1f} MB of "
+                f"{'KV bytes the waves request (reads of one context by several waves counted each time)' if args.prefill else 'algorithmic KV bytes'} "
+                f"(ratio {total / kv:.4f}).  Kernel source digest `{rec['source_digest']}`.\n")
     print(json.dumps({"bytes_per_call": rec["bytes_per_call"], "ratio_to_kv": total / kv}))
     return 0
 
