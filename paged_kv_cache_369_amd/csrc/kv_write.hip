@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict
             k = cov ? (e == 0 ? 2 : 3) : 1;
         }
         kind[tid] = uint8_t(k);
-        const unsigned long long m = __ballot(k == 2);  // kGroup == 64: one wave
+        const unsigned long long m = __ballot(k == 2);  // kGroup <= 64: one wave
         if (k == 2) heads[__builtin_popcountll(m & ((1ull << tid) - 1))] = tid;
         if (tid == 0) nheads = __builtin_popcountll(m);
     }
