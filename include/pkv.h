@@ -317,8 +317,9 @@ int paged_attention_varlen(void* out,
  *                clamp into [0, L_s]); tokens of a sequence at index
  *                >= max_q_len are not computed and their rows not written.
  * (no partition_size, no workspace)
- * Supported: G in {1, 2, 4, 8, 16}, head_dim 64 or 128, the dtype pairs of
- * paged_attention_decode; otherwise PKV_ERR_UNSUPPORTED (use
+ * Supported: G from 1 to 32 (a wave holds floor(32 / G) tokens; when G does
+ * not divide 32 the last columns stay empty), head_dim 64 or 128, the dtype
+ * pairs of paged_attention_decode; otherwise PKV_ERR_UNSUPPORTED (use
  * paged_attention_varlen).  Rows no sequence claims, or outside
  * [0, num_q_rows), are not written.
  * Errors: as paged_attention_varlen; PKV_ERR_INVALID_ARG also for

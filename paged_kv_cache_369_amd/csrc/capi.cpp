@@ -298,7 +298,7 @@ int paged_attention_prefill(void* out,
     if (int64_t(num_blocks) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
     if (int64_t(max_blocks_per_seq) * pkv::kBlockTokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARG;
     const int group = num_heads / num_kv_heads;
-    if (group > 16 || pkv::kPrefillWaveCols % group != 0) return PKV_ERR_UNSUPPORTED;
+    if (group > pkv::kPrefillWaveCols) return PKV_ERR_UNSUPPORTED;  // a wave holds at least one token
     if (int64_t(num_q_rows) * num_heads * head_dim >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
     const int tpw = pkv::kPrefillWaveCols / group;
     const int64_t items = int64_t(num_seqs) * num_kv_heads * ((int64_t(max_q_len) + tpw - 1) / tpw);

@@ -1334,7 +1334,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
     constexpr int CT = kPrefillTiles;
     const int lane = lane_id(), col = lane & 15;
     const int G = a.group;
-    const int tpw = kPrefillCols / G;  // new tokens per wave
+    const int tpw = kPrefillCols / G;  // new tokens per wave (columns past tpw * G hold none)
     // work item (sequence, KV head, token tile), token tile fastest; the
     // items of one XCD (workgroup w runs on XCD w mod 8) are consecutive
     const uint32_t per_xcd = gridDim.x / 8;

@@ -129,13 +129,14 @@ inline int64_t state_row_floats(int head_dim) { return int64_t(head_dim) + 4; }
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
-// Query columns of one prefill wave: kPrefillWaveCols / G new tokens times the
-// G query heads of one KV head (G must divide it and be at most 16).
+// Query columns of one prefill wave: floor(kPrefillWaveCols / G) new tokens
+// times the G query heads of one KV head (G at most kPrefillWaveCols; columns
+// past the last whole token stay empty).
 #ifndef PKV_PREFILL_COLS
 #define PKV_PREFILL_COLS 32
 #endif
 constexpr int kPrefillWaveCols = PKV_PREFILL_COLS;
-// Tiled prefill over `items` = num_seqs * num_kv_heads * ceil(max_q * G / kPrefillWaveCols) waves.
+// Tiled prefill over `items` = num_seqs * num_kv_heads * ceil(max_q / floor(kPrefillWaveCols / G)) waves.
 hipError_t launch_prefill(int cache_dtype, int head_dim, const DecodeArgs& a, int items, hipStream_t stream);
 
 struct CheckArgs {

@@ -223,8 +223,7 @@ def test_prefill_validation(lib):
     assert _pre(lib, cu=A + 2) == ALIGN
     assert _pre(lib, out=A + 8) == ALIGN
     assert _pre(lib, qd=0, cd=1) == UNSUPPORTED
-    assert _pre(lib, H=24, Hkv=8) == UNSUPPORTED                 # group 3 does not divide the 64 columns of a wave
-    assert _pre(lib, H=64, Hkv=2) == UNSUPPORTED                 # group 32 > 16
+    assert _pre(lib, H=66, Hkv=2) == UNSUPPORTED                 # group 33: a 32-column wave holds no token
     assert _pre(lib, D=96) == UNSUPPORTED
     assert _pre(lib, bs=32) == UNSUPPORTED
     assert _pre(lib, T=1 << 20, H=64, D=128) == UNSUPPORTED      # rows * heads * head_dim reach 2^31

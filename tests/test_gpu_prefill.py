@@ -43,6 +43,10 @@ def _prefill(w, kp, vp, max_q=None, cu=None, out=None):
     (16, 8, 64, "f32"),     # GQA 2
     (32, 2, 64, "bf16"),    # GQA 16: 2 tokens per wave
     (32, 8, 128, "f32"),
+    (24, 8, 128, "bf16"),   # GQA 3: 10 tokens per wave, two columns empty
+    (40, 8, 64, "fp8"),     # GQA 5: 6 tokens per wave
+    (24, 2, 64, "bf16"),    # GQA 12: 2 tokens per wave, eight columns empty
+    (32, 1, 128, "bf16"),   # GQA 32: 1 token per wave
 ])
 @pytest.mark.parametrize("pat", range(len(PATTERNS)))
 def test_prefill_parity(gpu, hq, hkv, d, cache, pat):
