@@ -101,7 +101,8 @@ __device__ __forceinline__ uint4 cache_chunk(const uint8_t* src, float scale) {
 
 // A group of kGroup consecutive tokens of one KV head per workgroup.
 //  1. The slots of the group, with CW - 1 tokens of context on each side
-//     (CW = 16 / CELT tokens fill 16 bytes of a dimension row of the V tile).
+//     (CW = 16 / CELT tokens fill 16 bytes of a dimension row of the V tile),
+//     requested together with the rows of step 2.
 //  2. Every K chunk of the group's tokens is loaded (coalesced along the
 //     token rows), converted and stored as one 16-byte write; the group's V
 //     rows (and the next CW - 1 tokens') are converted and transposed into
@@ -146,30 +147,44 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict
     const int t0 = int(blockIdx.x) * kGroup;
     const int h = int(blockIdx.y);
     const int tid = int(threadIdx.x);
-    // 1. slots (-1: none, past the batch, or outside the pool)
-    for (int i = tid; i < NSL; i += 256) {
-        const int tok = t0 - HALO + i;
-        const int s = (tok >= 0 && tok < num_tokens) ? slots[tok] : -1;
-        sl[i] = (s >= 0 && s < num_slots) ? s : -1;
-    }
-    __syncthreads();
-    // 2. K chunks of the group's tokens; V chunks of the group's tokens and the halo after it
+    // 1. the slots (-1: none, past the batch, or outside the pool) and 2. the
+    // K/V chunks are all requested before anything waits on them, so the
+    // slot reads and the row reads share one round trip
+    static_assert(NSL <= 256, "one slot per thread");
+    const int stok = t0 - HALO + tid;
+    const int sraw = (tid < NSL && stok >= 0 && stok < num_tokens) ? slots[stok] : -1;
+    constexpr int NIT = (NVT * CH + 255) / 256;  // chunk rows per thread
     const int nv = min(NVT, num_tokens - t0);
-    for (int i = tid; i < nv * CH; i += 256) {
-        const int tt = i / CH, c = i % CH;
-        const int64_t row = int64_t(t0 + tt) * num_kv_heads + h;
-        const int64_t src = (row * D + c * X) * IELT;
-        const int s = sl[tt + HALO];
-        if (tt < kGroup && s >= 0)
-            store_chunk(k_cache + k_chunk_offset(s, h, c, num_kv_heads, CH), cache_chunk<IN, CT>(k_new + src, k_scale));
-        const uint4 vx = cache_chunk<IN, CT>(v_new + src, v_scale);
-        const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+    uint4 kx[NIT], vx[NIT];
 #pragma unroll
-        for (int e = 0; e < X; ++e) {
-            uint8_t* dst = vt + (c * X + e) * PITCH + tt * CELT;
-            if constexpr (CELT == 4) *reinterpret_cast<uint32_t*>(dst) = w[e];
-            else if constexpr (CELT == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w[e / 2] >> (16 * (e % 2)));
-            else *dst = uint8_t(w[e / 4] >> (8 * (e % 4)));
+    for (int it = 0; it < NIT; ++it) {
+        const int i = tid + 256 * it;
+        if (i < nv * CH) {
+            const int tt = i / CH, c = i % CH;
+            const int64_t row = int64_t(t0 + tt) * num_kv_heads + h;
+            const int64_t src = (row * D + c * X) * IELT;
+            if (tt < kGroup) kx[it] = cache_chunk<IN, CT>(k_new + src, k_scale);
+            vx[it] = cache_chunk<IN, CT>(v_new + src, v_scale);
+        }
+    }
+    if (tid < NSL) sl[tid] = (sraw >= 0 && sraw < num_slots) ? sraw : -1;
+    __syncthreads();
+    // 2. K chunks of the group's tokens stored; V chunks of the group's tokens and the halo after it into LDS
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = tid + 256 * it;
+        if (i < nv * CH) {
+            const int tt = i / CH, c = i % CH;
+            const int s = sl[tt + HALO];
+            if (tt < kGroup && s >= 0) store_chunk(k_cache + k_chunk_offset(s, h, c, num_kv_heads, CH), kx[it]);
+            const uint32_t w[4] = {vx[it].x, vx[it].y, vx[it].z, vx[it].w};
+#pragma unroll
+            for (int e = 0; e < X; ++e) {
+                uint8_t* dst = vt + (c * X + e) * PITCH + tt * CELT;
+                if constexpr (CELT == 4) *reinterpret_cast<uint32_t*>(dst) = w[e];
+                else if constexpr (CELT == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(w[e / 2] >> (16 * (e % 2)));
+                else *dst = uint8_t(w[e / 4] >> (8 * (e % 4)));
+            }
         }
     }
     // 3a. what each token of the group does with its V elements; heads listed in token order
