@@ -667,9 +667,6 @@ __device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV
     }
 }
 
-// Two waves per SIMD (one for fp32 pools of head_dim 128, whose tiles and
-// query operands are twice as large): the matrix steps of one wave overlap the
-// softmax of the other.
 template <int KV, int D, bool CAUSAL>
 __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV, D>& t, int nv, int upto,
                                              const QOp<KV> (&qop)[Geo<KV, D>::NQ], Run<Geo<KV, D>::NVC>& rs) {
@@ -1322,6 +1319,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 constexpr int kPrefillCols = kPrefillWaveCols;
 constexpr int kPrefillTiles = kPrefillCols / 16;
 
+// Two waves per SIMD (one for fp32 pools of head_dim 128, whose tiles and
+// query operands are twice as large): the matrix steps of one wave overlap the
+// softmax of the other.
 template <int KV, int D>
 constexpr int kPrefillWaves = (KV == kF32 && D == 128) ? 1 : 2;
 
