@@ -209,6 +209,27 @@ def copy_calibration(torch, steps: int) -> int:
     return 0
 
 
+def read_ceiling(torch, pkv, nbytes: int, reps: int = 10) -> dict:
+    """A plain streaming read on the same GPU, beside the decode: pkv_stream_read over a buffer as large as the
+    decode's KV bytes (16-byte loads over a chip-filling grid).  Timed with events after two warm-ups."""
+    n16 = max(nbytes // 16, 1 << 16)
+    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(pkv.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pkv.pkv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pkv.pkv_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del buf
+    return {"GBps": 16 * n16 / us / 1e3, "bytes": 16 * n16, "avg_us": us,
+            "kernel": "pkv_stream_read over a buffer of the decode's KV size (a plain streaming read)"}
+
+
 def _csv_rows(directory: str, suffix: str):
     files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
     if not files:
@@ -508,6 +529,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cascade", action="store_true",
                     help="decode with paged_attention_decode_cascade using the workload's sharing arrays")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming-read measurement reported beside the decode's bandwidth")
     ap.add_argument("--prefill", action="store_true",
                     help="several-token workloads: time paged_attention_prefill (32 query columns per wave) "
                          "instead of paged_attention_varlen")
@@ -688,6 +711,7 @@ def main() -> int:
                      "traffic_source": traffic_src,
                      "kernel": "paged_decode_kernel (the whole decode call)",
                      "avg_us": dec_us,
+                     "p10_us": float(np.percentile(t_dec, 10)), "p90_us": float(np.percentile(t_dec, 90)),
                      "algorithmic_bytes_per_call": kv_bytes},
         "write_us": float(np.mean(t_write)),
         "attention_tokens_per_s": rows / (dec_us * 1e-6),
@@ -705,6 +729,11 @@ def main() -> int:
                               "kernel": "paged_prefill_kernel (the whole prefill call)", "avg_us": dec_us,
                               "algorithmic_flops_per_call": fl, "kv_read_bytes_bound": kv_bytes}
         log(f"prefill: {fl / 1e9:.1f} GFLOP per call -> {tf:.1f} TFLOP/s")
+
+    if not args.no_read_ceiling and result["roofline"]["bound"] == "hbm":
+        result["read_ceiling"] = read_ceiling(torch, pkv, kv_bytes)
+        log(f"plain streaming read on this GPU: {result['read_ceiling']['GBps']:.0f} GB/s "
+            f"(decode reaches {achieved / result['read_ceiling']['GBps']:.1%} of it)")
 
     if args.cpu_seqs != 0:
         n, nrows, dt, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)

@@ -337,6 +337,20 @@ int paged_attention_prefill(void* out,
                             void* stream);
 
 /*
+ * pkv_stream_read -- a plain streaming read of `bytes` bytes at `buf`
+ * (16-byte loads, each of PKV_STREAM_SINK_WORDS workgroups reading one
+ * contiguous share).  `sink` is a device array of PKV_STREAM_SINK_WORDS
+ * uint32 owned by the caller; the kernel may write any of them (in practice
+ * none).  A measurement aid: its rate is the same-GPU reference beside the
+ * decode's KV bandwidth.  Asynchronous on `stream`.
+ * Errors: PKV_ERR_INVALID_ARG (NULL pointers with bytes > 0),
+ * PKV_ERR_ALIGNMENT (buf or bytes not a multiple of 16, sink not 4-aligned),
+ * PKV_ERR_HIP.  bytes == 0 is a no-op.
+ */
+#define PKV_STREAM_SINK_WORDS 8192
+int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * pkv_check_inputs -- count the contents of the index arrays that the kernels
  * treat as invalid.  The write and decode stay memory-safe for any contents
  * (an out-of-range table entry is an empty block, a length is clamped into

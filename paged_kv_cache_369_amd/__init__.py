@@ -76,6 +76,8 @@ def _load():
     lib.paged_attention_prefill.argtypes = [p, p, ctypes.c_int, p, i32, i32, p, p, ctypes.c_int, p, i32, p,
                                             i32, i32, i32, i32, i32, i32, f32, f32, f32, p]
     lib.paged_attention_prefill.restype = ctypes.c_int
+    lib.pkv_stream_read.argtypes = [p, sz, p, p]
+    lib.pkv_stream_read.restype = ctypes.c_int
     lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
     lib.pkv_check_inputs.restype = ctypes.c_int
     i64 = ctypes.c_int64
@@ -331,6 +333,19 @@ def paged_attention_prefill(out, q, cu_seqlens_q, k_cache, v_cache, block_table,
                                      _dev(context_lens, "context_lens"), B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale),
                                      float(k_scale), float(v_scale), _stream(stream))
     _check(st, "paged_attention_prefill")
+
+
+STREAM_SINK_WORDS = 8192  # PKV_STREAM_SINK_WORDS in include/pkv.h
+
+
+def pkv_stream_read(buf, sink, stream=None) -> None:
+    """A plain streaming read of a device tensor (measurement aid); sink: int32 device tensor of
+    >= STREAM_SINK_WORDS elements."""
+    lib = _load()
+    if sink.numel() * sink.element_size() < 4 * STREAM_SINK_WORDS:
+        raise ValueError(f"sink needs {STREAM_SINK_WORDS} 32-bit words")
+    st = lib.pkv_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"), _stream(stream))
+    _check(st, "pkv_stream_read")
 
 
 def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_mapping=None, stream=None):

@@ -231,3 +231,12 @@ def test_prefill_validation(lib):
     assert _pre(lib, T=0) == OK
     assert _pre(lib, B=0) == OK
     assert _pre(lib, mq=0) == OK
+
+
+def test_stream_read_validation(lib):
+    assert lib.pkv_stream_read(A, 0, A, None) == OK               # nothing to read: no launch
+    assert lib.pkv_stream_read(0, 64, A, None) == INVALID
+    assert lib.pkv_stream_read(A, 64, 0, None) == INVALID
+    assert lib.pkv_stream_read(A + 8, 64, A, None) == ALIGN
+    assert lib.pkv_stream_read(A, 72, A, None) == ALIGN
+    assert lib.pkv_stream_read(A, 64, A + 2, None) == ALIGN
