@@ -52,3 +52,20 @@ def test_check_clean_workload_is_zero(gpu):
     got = pkv.pkv_check_inputs(w.layout.num_blocks, _gpu.to_dev(w.layout.block_table, "i32"),
                                _gpu.to_dev(w.context_lens, "i32"), _gpu.to_dev(w.layout.new_slots, "i32"))
     assert got == (0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 1 << 20, (1 << 20) + 48])
+def test_stream_read_runs_and_leaves_sink(gpu, nbytes):
+    """The plain-read measurement aid reads any multiple of 16 bytes (shares that end mid-row included) and,
+    for zero-filled data, writes nothing to its sink."""
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.full((pkv.STREAM_SINK_WORDS,), -1, dtype=torch.int32, device="cuda")
+    pkv.pkv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert bool((sink == -1).all())
+
+
+def test_stream_read_rejects_small_sink(gpu):
+    buf = torch.zeros(64, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        pkv.pkv_stream_read(buf, torch.zeros(16, dtype=torch.int32, device="cuda"))
