@@ -374,7 +374,8 @@ def utilisation(args) -> int:
 
 
 def summarize_counters(args) -> int:
-    """Markdown table of SQ/GRBM counters of the decode kernel (one or more --pmc runs)."""
+    """Markdown table of SQ/GRBM counters of the decode (or, with --prefill, the prefill) kernel (one or more
+    --pmc runs)."""
     vals = {}
     for d in args.counter_dirs:
         for r in _csv_rows(d, "counter_collection.csv"):
@@ -409,11 +410,18 @@ def summarize_counters(args) -> int:
     if "SQ_WAVE_CYCLES" in mean and mean.get("SQ_BUSY_CYCLES", 0) > 0:
         derived.append(f"- wave-cycles per busy SQ cycle (`SQ_WAVE_CYCLES / SQ_BUSY_CYCLES`): "
                        f"{mean['SQ_WAVE_CYCLES'] / mean['SQ_BUSY_CYCLES']:.2f}")
+    if "SQ_INSTS_MFMA" in mean and "SQ_WAVES" in mean and mean["SQ_WAVES"] > 0:
+        derived.append(f"- matrix instructions per wave (`SQ_INSTS_MFMA / SQ_WAVES`): "
+                       f"{mean['SQ_INSTS_MFMA'] / mean['SQ_WAVES']:.0f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("SQ_BUSY_CYCLES", 0) > 0:
+        derived.append(f"- matrix-busy cycles per busy SQ cycle (`SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES`): "
+                       f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mean['SQ_BUSY_CYCLES']:.3f}")
     if derived:
         lines += ["", "Ratios:", ""] + derived
     lines += ["", f"Decode source digest `{decode_source_digest()}`."]
     os.makedirs(args.out_dir, exist_ok=True)
-    path = os.path.join(args.out_dir, f"paged_decode_{profile_key(args)}_sq_counters.md")
+    stem = f"paged_prefill_{args.workload}" if args.prefill else f"paged_decode_{profile_key(args)}"
+    path = os.path.join(args.out_dir, f"{stem}_sq_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)

@@ -302,7 +302,9 @@ int paged_attention_prefill(void* out,
     if (int64_t(num_q_rows) * num_heads * head_dim >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
     const int tpw = pkv::kPrefillWaveCols / group;
     const int64_t items = int64_t(num_seqs) * num_kv_heads * ((int64_t(max_q_len) + tpw - 1) / tpw);
-    if (items + 8 >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+    // the grid deals pairs (sequence, KV head) to the 8 XCDs in equal numbers
+    if ((int64_t(num_seqs) * num_kv_heads + 7) / 8 * 8 * ((int64_t(max_q_len) + tpw - 1) / tpw) >= (int64_t(1) << 31))
+        return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_q_rows == 0 || max_q_len == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens || !cu_seqlens_q || (!block_table && max_blocks_per_seq > 0))
         return PKV_ERR_INVALID_ARG;

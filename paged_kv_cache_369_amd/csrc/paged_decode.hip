@@ -1335,16 +1335,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
     const int lane = lane_id(), col = lane & 15;
     const int G = a.group;
     const int tpw = kPrefillCols / G;  // new tokens per wave (columns past tpw * G hold none)
-    // work item (sequence, KV head, token tile), token tile fastest; the
-    // items of one XCD (workgroup w runs on XCD w mod 8) are consecutive
-    const uint32_t per_xcd = gridDim.x / 8;
-    const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    // Work item: (pair, token tile), a pair being (sequence, KV head).
+    // Workgroup w runs on XCD w mod 8 and is the (w / 8)-th item that XCD
+    // receives.  XCD x takes pairs x, x + 8, x + 16, ... in turn, all token
+    // tiles of a pair one after the other, so the waves reading one pair's
+    // context share an L2, and the pairs (the heads of a sequence included)
+    // are dealt round the XCDs rather than in contiguous ranges: XCDs given
+    // the long sequences no longer run on after the others.  A pair's last
+    // token tile, which sees the most context, goes first.
     const uint32_t ntt = uint32_t((a.max_q + tpw - 1) / tpw);
-    const int tt = int(item % ntt);
-    const uint32_t rest = item / ntt;
-    const int kvh = int(rest % uint32_t(a.num_kv_heads));
-    const int s = int(rest / uint32_t(a.num_kv_heads));
-    if (s >= a.num_seqs) return;
+    const uint32_t k = blockIdx.x / 8;
+    const uint32_t pair = blockIdx.x % 8 + 8 * (k / ntt);
+    const int tt = int(ntt - 1 - k % ntt);
+    if (pair >= uint32_t(a.num_seqs) * uint32_t(a.num_kv_heads)) return;
+    const int kvh = int(pair % uint32_t(a.num_kv_heads));
+    const int s = int(pair / uint32_t(a.num_kv_heads));
     const int L = clamped_len(a, s);
     const int q0 = a.cu_q[s];
     const int nq = min(max(a.cu_q[s + 1] - q0, 0), L);
@@ -1423,7 +1428,8 @@ hipError_t launch_prefill_t(const DecodeArgs& a, int items, hipStream_t stream) 
 #else
     constexpr int P = (KV == kF32 && D == 128) ? 2 : 3;
 #endif
-    const int grid = (items + 7) / 8 * 8;
+    const int pairs = a.num_seqs * a.num_kv_heads;  // items = pairs * token tiles per pair
+    const int grid = (pairs + 7) / 8 * 8 * (items / pairs);
     hipLaunchKernelGGL((paged_prefill_kernel<KV, D, P>), dim3(grid), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
