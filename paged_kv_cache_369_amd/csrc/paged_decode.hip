@@ -503,8 +503,30 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int64_t qr, bool hv,
     }
 }
 
-// Step 1: the K and V tiles of physical block `id`, KV head kvh.
-template <int KV, int D>
+// A load of 4, 8 or 16 bytes, plain or nontemporal.  Nontemporal loads carry
+// the streaming hint to the caches: a KV tile is read once per call, and on
+// MI355X a chip-wide stream of 8 KiB tiles read this way moves about 12 % more
+// bytes per second than with ordinary loads (6.7 against 6.0 TB/s).
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+template <typename T, bool NT>
+__device__ __forceinline__ T load_as(const uint8_t* p) {
+    if constexpr (!NT) {
+        return *reinterpret_cast<const T*>(p);
+    } else if constexpr (sizeof(T) == 16) {
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p)));
+    } else if constexpr (sizeof(T) == 8) {
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p)));
+    } else {
+        static_assert(sizeof(T) == 4, "4, 8 or 16 bytes");
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p)));
+    }
+}
+
+// Step 1: the K and V tiles of physical block `id`, KV head kvh (NT: with the
+// streaming hint, for tiles no other wave of the call reads).
+template <int KV, int D, bool NT>
 __device__ __forceinline__ void load_tile(const DecodeArgs& a, int kvh, int id, Tile<KV, D>& t) {
     using GE = Geo<KV, D>;
     const int lane = lane_id(), g = lane >> 4, col = lane & 15;
@@ -512,9 +534,9 @@ __device__ __forceinline__ void load_tile(const DecodeArgs& a, int kvh, int id, 
     const uint8_t* kt = static_cast<const uint8_t*>(a.k_cache) + off + lane * 16;
     const uint8_t* vt = static_cast<const uint8_t*>(a.v_cache) + off + (col * kBlockTokens + 4 * g) * GE::ELT;
 #pragma unroll
-    for (int u = 0; u < GE::NKL; ++u) t.k[u] = *reinterpret_cast<const uint4*>(kt + u * 1024);
+    for (int u = 0; u < GE::NKL; ++u) t.k[u] = load_as<uint4, NT>(kt + u * 1024);
 #pragma unroll
-    for (int c = 0; c < GE::NVC; ++c) t.v[c] = *reinterpret_cast<const VLoad<KV>*>(vt + c * 16 * kBlockTokens * GE::ELT);
+    for (int c = 0; c < GE::NVC; ++c) t.v[c] = load_as<VLoad<KV>, NT>(vt + c * 16 * kBlockTokens * GE::ELT);
 }
 
 // Running softmax state of one run inside the streaming loop, in the
@@ -687,6 +709,9 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const Tile<KV,
 // regions weigh 14 against 16.
 #ifndef PKV_ODD_XCD_WEIGHT
 #define PKV_ODD_XCD_WEIGHT 14
+#endif
+#ifndef PKV_ODD_XCD_WEIGHT8
+#define PKV_ODD_XCD_WEIGHT8 16
 #endif
 struct Split {
     uint32_t U, nw;
@@ -972,7 +997,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         }
     }
     Split sp;
-    sp.init(U, U < nwt ? U : nwt, KV == kFP8 ? 16u : uint32_t(PKV_ODD_XCD_WEIGHT));
+    sp.init(U, U < nwt ? U : nwt, KV == kFP8 ? uint32_t(PKV_ODD_XCD_WEIGHT8) : uint32_t(PKV_ODD_XCD_WEIGHT));
     if (w >= sp.nw) return;
     const uint32_t sw = sp.m ? (w % 8) * sp.m + w / 8 : w;  // this wave's stretch
     const uint32_t lo = sp.lo(sw), hi = sp.lo(sw + 1);
@@ -1162,7 +1187,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     // (a position past the stream loads block 0 of KV head 0 and counts no tokens)
     auto issue = [&](T& tb, int& nv, int& lraw, uint32_t pos) {
         int id = 0, kvh = 0, lim = 0;
-        bool real = false;
+        bool real = false, shared = false;
 #pragma unroll
         for (int k = 0; k < P; ++k) {
             if (!real && pos < sl[k].p1) {
@@ -1170,13 +1195,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 id = __builtin_amdgcn_readlane(sl[k].ids, off);
                 kvh = piece_hg(sl[k]) * a.rh / a.group;
                 lim = sl[k].lim0 - off * kBlockTokens;
+                shared = piece_kind(sl[k]) == 1;
                 real = true;
             }
         }
         const bool ok = real && id >= 0 && id < a.num_blocks;
         nv = ok ? min(kBlockTokens, lim) : 0;
         lraw = lim;
-        load_tile<KV, D>(a, ok ? kvh : 0, ok ? id : 0, tb);
+        if (M == kModeShared && shared)
+            load_tile<KV, D, false>(a, ok ? kvh : 0, ok ? id : 0, tb);
+        else
+            load_tile<KV, D, true>(a, ok ? kvh : 0, ok ? id : 0, tb);
     };
 
     __shared__ LdsState<NVC> held;  // merged state of the current run's finished partitions
@@ -1316,6 +1345,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 // holding neighbouring token tiles of one (sequence, KV head) are placed on
 // one XCD so their context reads meet in its L2.  No split over the
 // context: a wave keeps the softmax states of its columns to the end.
+#ifndef PKV_PREFILL_NT
+#define PKV_PREFILL_NT false
+#endif
 constexpr int kPrefillCols = kPrefillWaveCols;
 constexpr int kPrefillTiles = kPrefillCols / 16;
 
@@ -1392,7 +1424,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
         const int id = j < nblk ? __builtin_amdgcn_readlane(ids, j - jb) : -1;
         const bool ok = id >= 0 && id < a.num_blocks;
         nv = ok ? min(kBlockTokens, L - j * kBlockTokens) : 0;
-        load_tile<KV, D>(a, ok ? kvh : 0, ok ? id : 0, tb);
+        load_tile<KV, D, PKV_PREFILL_NT>(a, ok ? kvh : 0, ok ? id : 0, tb);
     };
     T buf[P];
     int nvb[P];
