@@ -51,6 +51,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 COPY_BYTES = 1 << 30
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+CPU_RUNS = 3  # timed oracle runs (after one warm-up); the median is reported
 WORKLOAD_DESC = {
     "tiny": "tiny fp32 paged decode: lens {7,16,33,100}, 4/4 heads, D=64",
     "13b": "LLaMA-2-13B-shaped bf16 decode: B=64, 40/40 heads, D=128, lens U[128,2048]",
@@ -502,25 +503,33 @@ def oracle_baseline(w, out_dev, q_dtype, max_seqs: int):
     else:
         n = min(max_seqs, w.num_seqs)
     sl = slice(0, n)
-    t0 = time.perf_counter()
-    if w.cu_q is not None:  # several new tokens per sequence: the rows of the first n sequences
-        rows = int(w.cu_q[n])
-        ref = oracle.paged_attention_varlen(np.ascontiguousarray(w.q[:rows]), w.q_dtype,
-                                            np.ascontiguousarray(w.cu_q[:n + 1]), kp, vp, w.cache_dtype,
-                                            np.ascontiguousarray(w.layout.block_table[sl]),
-                                            np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
-    else:
-        rows = n
-        ref = oracle.paged_attention(np.ascontiguousarray(w.q[sl]), w.q_dtype, kp, vp, w.cache_dtype,
-                                     np.ascontiguousarray(w.layout.block_table[sl]),
-                                     np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
-    dt = time.perf_counter() - t0
+    rows = int(w.cu_q[n]) if w.cu_q is not None else n
+
+    def run():
+        if w.cu_q is not None:  # several new tokens per sequence: the rows of the first n sequences
+            return oracle.paged_attention_varlen(np.ascontiguousarray(w.q[:rows]), w.q_dtype,
+                                                 np.ascontiguousarray(w.cu_q[:n + 1]), kp, vp, w.cache_dtype,
+                                                 np.ascontiguousarray(w.layout.block_table[sl]),
+                                                 np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale,
+                                                 w.v_scale)
+        return oracle.paged_attention(np.ascontiguousarray(w.q[sl]), w.q_dtype, kp, vp, w.cache_dtype,
+                                      np.ascontiguousarray(w.layout.block_table[sl]),
+                                      np.ascontiguousarray(w.context_lens[sl]), w.scale, w.k_scale, w.v_scale)
+
+    # one untimed warm-up, then the median of CPU_RUNS timed runs (wall clock, no generation or I/O inside)
+    ref = run()
+    times = []
+    for _ in range(CPU_RUNS):
+        t0 = time.perf_counter()
+        ref = run()
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     import torch
     o = out_dev[:rows].detach().cpu()
     got = (o.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32) \
         if q_dtype == "bf16" else o.numpy()
     err = float(np.max(np.abs(got.astype(np.float64) - ref))) if ref.size else 0.0
-    return n, rows, dt, oracle.num_threads(0), err
+    return n, rows, dt, times, oracle.num_threads(0), err
 
 
 def main() -> int:
@@ -744,12 +753,16 @@ def main() -> int:
             f"(decode reaches {achieved / result['read_ceiling']['GBps']:.1%} of it)")
 
     if args.cpu_seqs != 0:
-        n, nrows, dt, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)
+        n, nrows, dt, times, cores, err = oracle_baseline(w, out, w.q_dtype, args.cpu_seqs)
         tok = int(w.context_lens[:n].sum())
+        sample_kv = tok * w.num_kv_heads * w.head_dim * 2 * w.kv_elt_bytes()  # each sampled context once
         result["cpu_baseline"] = {
             "value": nrows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {w.num_seqs} sequences of this workload ({nrows} query tokens, all {w.num_heads} "
-                      f"heads, {tok} context tokens, one step), {dt:.2f} s wall on {cores} threads of {cpu_model()}",
+                      f"heads, {tok} context tokens, one step); median of {CPU_RUNS} timed runs after one "
+                      f"warm-up, {dt:.2f} s each, on {cores} threads of {cpu_model()}",
+            "GBps": sample_kv / dt / 1e9, "kv_bytes": sample_kv, "runs": CPU_RUNS, "warmup": 1,
+            "run_s": [round(t, 4) for t in times], "median_s": dt, "cpu_model": cpu_model(),
         }
         result["check"] = {"max_abs_err_vs_oracle": err, "tolerance": TOL[w.cache_dtype], "seqs": n,
                            "pass": bool(err <= TOL[w.cache_dtype])}

@@ -27,7 +27,12 @@
  *    the sizes describe: a table entry outside [0, num_blocks) makes its
  *    block count as empty, a length outside [0, max_blocks_per_seq*16] is
  *    clamped into that range, a slot outside [-1, num_blocks*16) is skipped.
- *    Results for such inputs are unspecified (but memory-safe).
+ *    Results for such inputs are unspecified (but memory-safe).  This holds in
+ *    every build: there is no separate debug build, no device error word and
+ *    no debug-check call.  The validation entry point is pkv_check_inputs,
+ *    one small launch that counts the contents the kernels would treat as
+ *    invalid; a caller that wants the check runs it beside (or before) the
+ *    calls whose inputs it covers.
  *  - All device pointers must be 16-byte aligned (PKV_ERR_ALIGNMENT).
  *  - block_size must be 16; head_dim must be 64 or 128; num_heads must be a
  *    multiple of num_kv_heads.  Supported (q, cache) dtype pairs for decode:
@@ -71,12 +76,17 @@ typedef enum pkv_status {
     PKV_ERR_OUT_OF_BLOCKS = 6 /* the block manager has too few free blocks (nothing was changed) */
 } pkv_status;
 
-/* Version of this ABI (incremented on any incompatible change; 2 = the
- * chunked-K / dimension-major-V pool layout and the workspace query that
- * takes num_kv_heads; 3 = the workspace must be zero-filled before its first
- * use and is left that way by every call; 4 = the block manager and
- * paged_kv_copy_blocks; 5 = paged_attention_decode_cascade; 6 =
- * paged_attention_varlen; 7 = the block manager's prefix caching). */
+/* Version of this ABI, incremented on any incompatible change or added
+ * entry point:
+ *   2 = the chunked-K / dimension-major-V pool layout, and the workspace
+ *       query takes num_kv_heads;
+ *   3 = the workspace must be zero-filled before its first use and is left
+ *       that way by every call;
+ *   4 = the block manager and paged_kv_copy_blocks;
+ *   5 = paged_attention_decode_cascade;
+ *   6 = paged_attention_varlen;
+ *   7 = the block manager's prefix caching;
+ *   8 = paged_attention_prefill. */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -118,7 +128,10 @@ int paged_kv_write(const void* k_new, const void* v_new, int in_dtype,
  * workspace holds arrival counters and the partial softmax states of the runs
  * (sequence, group of query heads sharing a KV head) that the balanced work
  * split cuts between waves: two states per persistent wave (at most 4096
- * waves), so the size depends on the head grouping and head_dim only.
+ * waves), so the size depends on the head grouping and head_dim only.  The
+ * query takes num_kv_heads for that reason: a state holds one column per
+ * query head of a run, and the heads per run follow from the group size
+ * num_heads / num_kv_heads (the largest divisor of it that is at most 16).
  * partition_size as in paged_attention_decode.  Returns 0 for arguments
  * paged_attention_decode would reject.
  */
@@ -338,8 +351,8 @@ int paged_attention_prefill(void* out,
 
 /*
  * pkv_stream_read -- a plain streaming read of `bytes` bytes at `buf`
- * (16-byte loads, each of PKV_STREAM_SINK_WORDS workgroups reading one
- * contiguous share).  `sink` is a device array of PKV_STREAM_SINK_WORDS
+ * (16-byte nontemporal loads, each of PKV_STREAM_SINK_WORDS workgroups
+ * reading one contiguous share).  `sink` is a device array of PKV_STREAM_SINK_WORDS
  * uint32 owned by the caller; the kernel may write any of them (in practice
  * none).  A measurement aid: its rate is the same-GPU reference beside the
  * decode's KV bandwidth.  Asynchronous on `stream`.
@@ -356,8 +369,11 @@ int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream)
  * (an out-of-range table entry is an empty block, a length is clamped into
  * [0, max_blocks_per_seq*16], an out-of-range slot is skipped), so their
  * results are simply unspecified for such inputs; this call says whether that
- * happened.  A debug aid: one workgroup, and the repeat check is quadratic in
- * num_tokens.
+ * happened.  It is the boundary's validation call (there is no debug build
+ * or device error word).  Two launches: one workgroup for the lengths, table
+ * entries and slot ranges, then ceil(num_tokens / 4096) workgroups that find
+ * repeated slots through hash tables in LDS (linear in num_tokens for any
+ * practical input).
  *   Source for what is valid: ipipp.com article §二 (the table maps each
  *   logical block to a physical one); bytelighting wiki "vLLM", "Flattened
  *   布局与 slot_mapping" (one slot per new token).

@@ -197,16 +197,22 @@ def paged_attention_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads:
 _WORKSPACES = {}
 
 
-def _default_workspace(device, need: int):
-    """A zero-filled workspace per device, grown on demand.  The decode leaves
-    its counters at zero, so the buffer is reused without clearing; calls on
-    different streams of one device that use it must not overlap (pass a
-    workspace of your own for that)."""
+def _default_workspace(device, need: int, stream=None):
+    """A zero-filled workspace per (device, stream), grown on demand.
+
+    It is allocated and zero-filled on the stream the call runs on, so the
+    fill is ordered before the kernel that first reads it, and the caching
+    allocator keeps the memory for that stream (a buffer dropped when the
+    workspace grows is reused only by later work on the same stream).  The
+    decode leaves its counters at zero, so the buffer is reused without
+    clearing.  Calls on different streams get different buffers."""
     import torch
-    key = (device.type, device.index)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.type, device.index, int(s.cuda_stream))
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -217,8 +223,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the paged context of sequence s.
 
     workspace: uint8 device tensor of at least paged_attention_workspace_bytes(...)
-    bytes, zero-filled before its first use (torch.zeros); None uses a shared
-    per-device buffer."""
+    bytes, zero-filled before its first use (torch.zeros); None uses a buffer
+    the binding keeps per (device, stream), allocated and zeroed on that stream."""
     import torch
     lib = _load()
     B, Hq, D = q.shape
@@ -230,7 +236,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
     MB = block_table.shape[1]
     need = paged_attention_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
     if workspace is None and need > 0:
-        workspace = _default_workspace(q.device, need)
+        workspace = _default_workspace(q.device, need, stream)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.paged_attention_decode(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),
@@ -267,7 +273,7 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_table, contex
     MB = block_table.shape[1]
     need = paged_attention_cascade_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
     if workspace is None and need > 0:
-        workspace = _default_workspace(q.device, need)
+        workspace = _default_workspace(q.device, need, stream)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.paged_attention_decode_cascade(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),
@@ -303,7 +309,7 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
     MB = block_table.shape[1]
     need = paged_attention_varlen_workspace_bytes(B, Hq, Hkv, D, MB, BLOCK_SIZE, partition_size)
     if workspace is None and need > 0:
-        workspace = _default_workspace(q.device, need)
+        workspace = _default_workspace(q.device, need, stream)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.paged_attention_varlen(_dev(out, "out"), _dev(q, "q"), _dtype_code(q), _dev(cu_seqlens_q, "cu_seqlens_q"),
@@ -365,6 +371,8 @@ def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_
                                   _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else none, T,
                                   int(num_blocks), _dev(counts, "counts"), _stream(stream))
     _check(st, "pkv_check_inputs")
+    if stream is not None:
+        stream.synchronize()  # the counts are written on `stream`; .cpu() below waits on torch's current one
     return tuple(int(x) for x in counts.cpu().tolist())
 
 

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
     const int tid = threadIdx.x;
     if (tid < 4) cnt[tid] = 0;
     __syncthreads();
-    int bad_len = 0, bad_entry = 0, bad_slot = 0, dup_slot = 0;
+    int bad_len = 0, bad_entry = 0, bad_slot = 0;
     // context lengths
     for (int s = tid; s < a.num_seqs; s += kCheckThreads) {
         const int L = a.context_lens[s];
@@ -37,32 +37,90 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
             bad_entry += (id < 0 || id >= a.num_blocks) ? 1 : 0;
         }
     }
-    // slots: -1 or in range; an in-range slot equal to an earlier one is a repeat
+    // slots: -1 or in range (repeats are counted by repeat_kernel, launched after this one)
     const int64_t nslots = int64_t(a.num_blocks) * kBlockTokens;
     for (int i = tid; i < a.num_tokens; i += kCheckThreads) {
         const int sl = a.slot_mapping[i];
         bad_slot += (sl == -1 || (sl >= 0 && sl < nslots)) ? 0 : 1;
-        if (sl >= 0) {
+    }
+    atomicAdd(&cnt[0], bad_len);
+    atomicAdd(&cnt[1], bad_entry);
+    atomicAdd(&cnt[2], bad_slot);
+    __syncthreads();
+    if (tid < 4) a.counts[tid] = cnt[tid];  // counts[3] = 0 here; repeat_kernel adds to it
+}
+
+// Repeated slots.  The values >= 0 are split into `parts` classes by a hash;
+// workgroup p reads every slot, inserts those of class p into an LDS hash
+// table (linear probing, compare-and-swap), and counts an insertion that
+// finds its value already there.  Each value with k occurrences thus adds
+// k - 1, the number of entries that repeat an earlier one.  The host picks
+// parts so that a class holds about kRepeatLoad distinct values, well under
+// the table's kRepeatTable entries.  A value that finds the table full
+// (possible only if the hash is defeated) is checked by a scan of the
+// entries before it instead, which gives the same count: a value is then
+// absent from the table for good, so all its occurrences take that path.
+constexpr int kRepeatTable = 16384;  // LDS entries (64 KiB)
+constexpr uint32_t kEmpty = 0xffffffffu;
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x, uint32_t seed) {  // murmur3 finaliser of x ^ seed
+    x ^= seed;
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return x;
+}
+
+__global__ __launch_bounds__(kCheckThreads) void repeat_kernel(const int32_t* slots, int32_t n, uint32_t parts,
+                                                               int32_t* counts) {
+    __shared__ uint32_t tab[kRepeatTable];
+    __shared__ int dup;
+    const int tid = threadIdx.x;
+    for (int k = tid; k < kRepeatTable; k += kCheckThreads) tab[k] = kEmpty;
+    if (tid == 0) dup = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int i = tid; i < n; i += kCheckThreads) {
+        const int sl = slots[i];
+        if (sl < 0 || mix32(uint32_t(sl), 0x9e3779b9u) % parts != blockIdx.x) continue;
+        const uint32_t v = uint32_t(sl);
+        uint32_t b = mix32(v, 0x7f4a7c15u) & (kRepeatTable - 1);
+        bool placed = false;
+        for (int probe = 0; probe < kRepeatTable; ++probe, b = (b + 1) & (kRepeatTable - 1)) {
+            const uint32_t old = atomicCAS(&tab[b], kEmpty, v);
+            if (old == kEmpty || old == v) {
+                mine += old == v ? 1 : 0;
+                placed = true;
+                break;
+            }
+        }
+        if (!placed) {  // the table is full and does not hold v: an exact scan of the earlier entries
             for (int j = 0; j < i; ++j) {
-                if (a.slot_mapping[j] == sl) {
-                    ++dup_slot;
+                if (slots[j] == sl) {
+                    ++mine;
                     break;
                 }
             }
         }
     }
-    atomicAdd(&cnt[0], bad_len);
-    atomicAdd(&cnt[1], bad_entry);
-    atomicAdd(&cnt[2], bad_slot);
-    atomicAdd(&cnt[3], dup_slot);
+    atomicAdd(&dup, mine);
     __syncthreads();
-    if (tid < 4) a.counts[tid] = cnt[tid];
+    if (tid == 0 && dup > 0) atomicAdd(&counts[3], dup);
 }
 
 }  // namespace
 
+constexpr int kRepeatLoad = 4096;  // distinct values per hash class the host aims for
+
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(check_kernel, dim3(1), dim3(kCheckThreads), 0, stream, a);
+    if (a.num_tokens > 0) {
+        const uint32_t parts = uint32_t((int64_t(a.num_tokens) + kRepeatLoad - 1) / kRepeatLoad);
+        hipLaunchKernelGGL(repeat_kernel, dim3(parts), dim3(kCheckThreads), 0, stream, a.slot_mapping, a.num_tokens,
+                           parts, a.counts);
+    }
     return hipGetLastError();
 }
 
@@ -70,13 +128,15 @@ hipError_t launch_check(const CheckArgs& a, hipStream_t stream) {
 
 // ---- a plain streaming read (measurement aid) ----
 //
-// Reads a buffer once with 16-byte loads.  Each of 8192 workgroups (32 per
-// compute unit) streams its own contiguous share, four loads in flight per
-// thread, and folds the words into one value that is stored only if it
-// matches a constant (so the loads are kept and almost nothing is written).
-// Of the shapes timed (grid-stride or contiguous shares, 2048 to 8192
-// workgroups, 4 to 16 loads in flight) this one read fastest.  Its rate is
-// the same-GPU reference the decode's KV bandwidth is set beside.
+// Reads a buffer once with 16-byte nontemporal loads (the streaming hint: on
+// MI355X a once-read stream moves about 12 % more bytes per second with it
+// than with ordinary loads).  Each of 8192 workgroups (32 per compute unit)
+// streams its own contiguous share, four loads in flight per thread, and
+// folds the words into one value that is stored only if it matches a
+// constant (so the loads are kept and almost nothing is written).  Of the
+// shapes timed (grid-stride or contiguous shares, 2048 to 8192 workgroups,
+// 4 to 16 loads in flight) this one read fastest.  Its rate is the same-GPU
+// reference the decode's KV bandwidth is set beside.
 namespace pkv {
 namespace {
 
@@ -91,16 +151,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     const int64_t b0 = int64_t(blockIdx.x) * per;
     const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
     int64_t i = b0 + threadIdx.x;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
     for (; i + (kStreamInFlight - 1) * kStreamThreads < b1; i += kStreamInFlight * kStreamThreads) {
-        uint4 v[kStreamInFlight];
+        u32x4 v[kStreamInFlight];
 #pragma unroll
-        for (int k = 0; k < kStreamInFlight; ++k) v[k] = p[i + k * kStreamThreads];
+        for (int k = 0; k < kStreamInFlight; ++k) v[k] = __builtin_nontemporal_load(q + i + k * kStreamThreads);
 #pragma unroll
-        for (int k = 0; k < kStreamInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+        for (int k = 0; k < kStreamInFlight; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
     }
     for (; i < b1; i += kStreamThreads) {
-        const uint4 a = p[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        const u32x4 a = __builtin_nontemporal_load(q + i);
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
     if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }

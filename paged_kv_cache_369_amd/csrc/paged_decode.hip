@@ -382,6 +382,34 @@ __device__ __forceinline__ uint32_t seq_units(const DecodeArgs& a, const SeqInfo
     return uint32_t(nb - si.pbe + (si.cl == s ? si.pbe : 0)) * uint32_t(a.runs);
 }
 
+// The same count in 64 bits, for the guard against totals the 32-bit unit
+// line cannot hold (possible only for contents the host does not check, such
+// as a cu_seqlens_q that decreases).
+template <int M>
+__device__ __forceinline__ uint64_t seq_units64(const DecodeArgs& a, const SeqInfo& si, int s) {
+    if constexpr (M == kModeMulti) {
+        uint64_t b = 0;
+        for (int g = 0; g * a.members < si.nq; ++g) b += uint64_t(group_blocks(si.len, si.nq, a.members, g));
+        return b * uint64_t(a.runs);
+    }
+    const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
+    return uint64_t(nb - si.pbe + (si.cl == s ? si.pbe : 0)) * uint64_t(a.runs);
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor(uint32_t(x), off), hi = __shfl_xor(uint32_t(x >> 32), off);
+        x += (uint64_t(hi) << 32) | lo;
+    }
+    return x;
+}
+
+// Unit totals at or above this bound are refused by the kernel (every wave
+// returns without a write): the unit line and its cursors use 32-bit
+// positions, and the host's size check keeps valid inputs below it.
+constexpr uint64_t kMaxUnits = uint64_t(1) << 31;
+
 // Forward cursor over the sequences, 64 at a time: lane i holds sequence
 // base + i.
 struct Cursor {
@@ -974,6 +1002,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     // ---- total units; per-chunk totals of the first kLenChunks chunks; rows
     //      of empty sequences are zeroed (sequence s by wave s mod grid) ----
     uint32_t U = 0;
+    uint64_t U64 = 0;  // the same total, without wrap-around
     uint32_t ctot[kLenChunks];
 #pragma unroll
     for (int c = 0; c < kLenChunks; ++c) ctot[c] = 0;
@@ -986,6 +1015,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             const int cb = base + 64 * c;
             if (cb >= a.num_seqs) break;
             const uint32_t t = __builtin_amdgcn_readlane(wave_scan(seq_units<M>(a, si[c], cb + lane)), 63);
+            U64 += wave_sum64(seq_units64<M>(a, si[c], cb + lane));
             if (base == 0) ctot[c] = t;
             U += t;
             unsigned long long empty = __ballot(M != kModeMulti && cb + lane < a.num_seqs && si[c].len == 0);
@@ -996,6 +1026,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
     }
+    // Past the bound the 32-bit positions below could wrap: every wave returns
+    // here.  Only several-query calls can get here (their per-sequence counts
+    // come from cu_seqlens_q), and those write nothing before this point, so
+    // the output and the workspace stay untouched.
+    if (U64 >= kMaxUnits) return;
     Split sp;
     sp.init(U, U < nwt ? U : nwt, KV == kFP8 ? uint32_t(PKV_ODD_XCD_WEIGHT8) : uint32_t(PKV_ODD_XCD_WEIGHT));
     if (w >= sp.nw) return;

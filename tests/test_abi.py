@@ -41,6 +41,12 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pkv_abi_version() == 8
+    # the header's version history names every version up to the current one
+    text = open(HEADER).read()
+    hist = text[text.index("Version of this ABI"):text.index("int pkv_abi_version(void);")]
+    for v in range(2, lib.pkv_abi_version() + 1):
+        assert re.search(rf"\b{v} = ", hist), f"ABI history in pkv.h does not name version {v}"
+    assert not re.search(rf"\b{lib.pkv_abi_version() + 1} = ", hist), "ABI history names a version past the library's"
     for st in range(7):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"

@@ -69,3 +69,32 @@ def test_stream_read_rejects_small_sink(gpu):
     buf = torch.zeros(64, dtype=torch.int32, device="cuda")
     with pytest.raises(ValueError):
         pkv.pkv_stream_read(buf, torch.zeros(16, dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("case", ["many_tokens", "one_value", "consecutive"])
+def test_check_repeats_at_chunk_sizes(gpu, case):
+    """Repeated slots among tens of thousands of tokens (several hash classes, one workgroup each): values
+    repeated up to six times, one value repeated everywhere, and whole chunks of consecutive slots."""
+    rng = np.random.default_rng(7)
+    NB = 20000
+    if case == "many_tokens":
+        T = 70000
+        slots = rng.permutation(NB * 16)[:T].astype(np.int32)
+        src = rng.integers(0, T, 9000)
+        dst = rng.integers(0, T, 9000)
+        slots[dst] = slots[src]  # repeats (some chained), anywhere in the array
+        slots[rng.choice(T, 500, replace=False)] = -1
+        slots[rng.choice(T, 50, replace=False)] = NB * 16 + 3
+    elif case == "one_value":
+        T = 20000
+        slots = np.full(T, 4242, np.int32)
+    else:
+        T = 16 * 512
+        slots = (np.arange(T) + 64).astype(np.int32)
+        slots[4096:] = slots[:4096]  # the second half of the chunk repeats the first
+    bt = np.zeros((1, 1), np.int32)
+    cl = np.zeros(1, np.int32)
+    want = _expected(bt, cl, slots, NB)
+    _gpu.note(f"check_inputs repeats case={case} T={T} want={want}")
+    got = pkv.pkv_check_inputs(NB, _gpu.to_dev(bt, "i32"), _gpu.to_dev(cl, "i32"), _gpu.to_dev(slots, "i32"))
+    assert got == want

@@ -113,3 +113,31 @@ def test_long_chunk_merge_tree(gpu):
     want = _gpu.oracle_varlen(w, w.layout, ok, ov)
     err, where = _gpu.max_err(got, want)
     assert err <= _gpu.TOL["bf16"], (err, where)
+
+
+def test_units_past_the_32bit_line_leave_everything_unwritten(gpu):
+    """cu_seqlens_q that keeps growing past num_q_rows gives every sequence its whole context as new tokens.
+    The host's size check (which assumes counts summing to at most num_q_rows) passes, but the unit total
+    passes 2^32 and would wrap to a small number in 32 bits; the kernel counts units in 64 bits and returns
+    before writing anything."""
+    B, Hq, Hkv, D, L, rows = 64, 32, 8, 128, 32768, 32768
+    mb, members, runs = L // 16, 4, Hq // 4
+    # host bound (capi.cpp): (rows / members + B) * runs * max_blocks < 2^31
+    assert (rows // members + B) * runs * mb < 2 ** 31
+    # units the kernel counts per sequence with n = L new tokens: every group of 4 reads ceil(last token / 16)
+    per_seq = sum(-(-min(members * (g + 1), L) // 16) for g in range(L // members)) * runs
+    assert B * per_seq >= 2 ** 32 and (B * per_seq) % 2 ** 32 < 2 ** 31  # the 32-bit total wraps below the bound
+    nb = 1
+    kc = torch.zeros(pkv.k_cache_shape(nb, Hkv, D, "bf16"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(pkv.v_cache_shape(nb, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(rows, Hq, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    cu = torch.arange(B + 1, dtype=torch.int32, device="cuda") * L
+    bt = torch.zeros(B, mb, dtype=torch.int32, device="cuda")
+    cl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(pkv.paged_attention_varlen_workspace_bytes(B, Hq, Hkv, D, mb), dtype=torch.uint8, device="cuda")
+    _gpu.note("varlen with a unit total past 2^32 (malformed cu_seqlens_q)")
+    pkv.paged_attention_varlen(out, q, cu, kc, vc, bt, cl, 0.088, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out.float()).all()), "rows were written"
+    assert int(torch.count_nonzero(ws)) == 0
