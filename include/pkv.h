@@ -73,7 +73,8 @@ typedef enum pkv_status {
     PKV_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned */
     PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than paged_attention_workspace_bytes() */
     PKV_ERR_HIP = 5,          /* the HIP runtime reported an error while launching */
-    PKV_ERR_OUT_OF_BLOCKS = 6 /* the block manager has too few free blocks (nothing was changed) */
+    PKV_ERR_OUT_OF_BLOCKS = 6, /* the block manager has too few free blocks (nothing was changed) */
+    PKV_ERR_SCRATCH = 7        /* paged_attention_decode_noalloc: its static scratch is too small for these sizes */
 } pkv_status;
 
 /* Version of this ABI, incremented on any incompatible change or added
@@ -86,7 +87,8 @@ typedef enum pkv_status {
  *   5 = paged_attention_decode_cascade;
  *   6 = paged_attention_varlen;
  *   7 = the block manager's prefix caching;
- *   8 = paged_attention_prefill. */
+ *   8 = paged_attention_prefill;
+ *   9 = paged_attention_decode_noalloc and PKV_ERR_SCRATCH. */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -192,6 +194,43 @@ int paged_attention_decode(void* out,
                            int32_t partition_size,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * paged_attention_decode_noalloc -- paged_attention_decode with no workspace
+ * argument and no allocation of any kind.  For callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.
+ *
+ * The decode's workspace (arrival counters and the partial softmax states of
+ * runs cut between waves) lives in a static device array of the library,
+ * PKV_NOALLOC_SCRATCH_BYTES long, one per GPU, held from the first call on
+ * that GPU until the process ends.  The first call on a device takes the
+ * array's address and clears its counters with a small fill kernel on that
+ * call's stream; every call that completes leaves them at zero again.
+ * Arguments, results and errors as paged_attention_decode (same kernel, same
+ * result bits), plus PKV_ERR_SCRATCH, returned before anything is launched,
+ * when the states of the persistent waves do not fit: the counters (about
+ * 1.1 MB) plus two states of 32 + run_heads * head_dim floats per wave, with
+ * run_heads the largest divisor of num_heads / num_kv_heads that is at most
+ * 16 and 2048 waves on MI355X for 16-bit and 8-bit pools.  So every shape
+ * with run_heads <= 8 fits at head_dim 128 (18 MB at 8), and run_heads 16 at
+ * head_dim 128 does not (35 MB).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams without ordering between them, or from several
+ * threads) race and give unspecified results.  Calls on one stream are
+ * ordered and safe.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paged_attention_decode_noalloc(void* out,
+                                   const void* q, int q_dtype,
+                                   const void* k_cache, const void* v_cache, int cache_dtype,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   float scale, float k_scale, float v_scale,
+                                   int32_t partition_size,
+                                   void* stream);
 
 /*
  * paged_attention_cascade_workspace_bytes -- workspace size for

@@ -25,6 +25,7 @@ import ctypes
 import os
 
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
+           "paged_attention_decode_noalloc",
            "BlockManager", "paged_kv_copy_blocks", "paged_attention_varlen", "paged_attention_prefill",
            "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
@@ -63,6 +64,9 @@ def _load():
     lib.paged_attention_decode.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p,
                                            i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p, sz, p]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p,
+                                                   i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, p]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.paged_attention_cascade_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_attention_cascade_workspace_bytes.restype = sz
     lib.paged_attention_decode_cascade.argtypes = [p, p, ctypes.c_int, p, p, ctypes.c_int, p, i32, p, p, p,
@@ -245,6 +249,31 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
                                     B, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), float(k_scale), float(v_scale),
                                     int(partition_size), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "paged_attention_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_table, context_lens, scale: float,
+                                   k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                                   stream=None) -> None:
+    """paged_attention_decode with the library's static per-GPU scratch as its workspace: no workspace
+    argument and no allocation (see include/pkv.h).  Calls that overlap on one GPU race."""
+    lib = _load()
+    B, Hq, D = q.shape
+    NB, Hkv, Dc = _pools(k_cache, v_cache)
+    if out.shape != q.shape or Dc != D:
+        raise ValueError("shape mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and context_lens [B]")
+    MB = block_table.shape[1]
+    st = lib.paged_attention_decode_noalloc(_dev(out, "out"), _dev(q, "q"), _dtype_code(q),
+                                            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                            _dtype_code(k_cache), _dev(block_table, "block_table"), MB,
+                                            _dev(context_lens, "context_lens"), B, Hq, Hkv, D, BLOCK_SIZE, NB,
+                                            float(scale), float(k_scale), float(v_scale), int(partition_size),
+                                            _stream(stream))
+    _check(st, "paged_attention_decode_noalloc")
 
 
 def paged_attention_cascade_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,

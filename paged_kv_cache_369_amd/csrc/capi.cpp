@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -30,6 +30,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_SCRATCH: return "the no-allocation decode's static scratch is too small for these sizes";
     default: return "unknown status";
     }
 }
@@ -98,7 +99,7 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 float scale, float k_scale, float v_scale, int32_t partition_size, const int32_t* prefix_leader,
                 const int32_t* prefix_blocks, bool cascade, const int32_t* cu_q, int32_t num_q_rows, bool multi,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         num_blocks < 0 || max_blocks_per_seq < 0)
         return PKV_ERR_INVALID_ARG;
@@ -138,14 +139,26 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
         !aligned(prefix_leader, 4) || !aligned(prefix_blocks, 4) || !aligned(cu_q, 4))
         return PKV_ERR_ALIGNMENT;
 
-    const size_t need =
-        cascade ? paged_attention_cascade_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                          max_blocks_per_seq, block_size, partition_size)
-        : multi ? paged_attention_varlen_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                         max_blocks_per_seq, block_size, partition_size)
-                : paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                                                  block_size, partition_size);
-    if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (noalloc) {
+        // The plain decode with the library's static scratch as its workspace: the counters, then two
+        // partial-state slots per wave the launch runs.  Sizes whose slots do not fit are refused here,
+        // before anything is launched.
+        const int64_t need = (pkv::kSlotBase + 2 * int64_t(pkv::decode_waves(cache_dtype, head_dim)) *
+                                                   pkv::slot_floats(rh, head_dim)) * int64_t(sizeof(float));
+        if (need > int64_t(pkv::kNoAllocScratchBytes)) return PKV_ERR_SCRATCH;
+        float* ws = nullptr;
+        if (pkv::noalloc_scratch(&ws, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+        workspace = ws;
+    } else {
+        const size_t need =
+            cascade ? paged_attention_cascade_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                              max_blocks_per_seq, block_size, partition_size)
+            : multi ? paged_attention_varlen_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                             max_blocks_per_seq, block_size, partition_size)
+                    : paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                      max_blocks_per_seq, block_size, partition_size);
+        if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    }
 
     pkv::DecodeArgs a{};
     a.out = out;
@@ -212,6 +225,21 @@ int paged_attention_decode(void* out,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
                        partition_size, nullptr, nullptr, false, nullptr, 0, false, workspace, workspace_bytes,
                        stream);
+}
+
+int paged_attention_decode_noalloc(void* out,
+                                   const void* q, int q_dtype,
+                                   const void* k_cache, const void* v_cache, int cache_dtype,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   float scale, float k_scale, float v_scale,
+                                   int32_t partition_size,
+                                   void* stream) {
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
+                       partition_size, nullptr, nullptr, false, nullptr, 0, false, nullptr, 0, stream, true);
 }
 
 size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -54,6 +54,7 @@
 // select, so poisoned memory never reaches an accumulator.  Padding table
 // entries are never read.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -1350,22 +1351,30 @@ int device_cus() {
     return cached;
 }
 
+// Persistent waves one launch of this instance runs: its occupancy (one-wave
+// workgroups per CU) times the CUs, at most kMaxWaves.
 template <int KV, int D, int M>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+int waves_t() {
     constexpr int P = Depth<KV, D>::P;
-    auto kern = paged_decode_kernel<KV, D, P, M>;
-    static int waves_per_cu = 0;  // occupancy of this instance (64-thread workgroups)
+    static int waves_per_cu = 0;
     if (waves_per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64, 0) != hipSuccess || n <= 0) n = 8;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, paged_decode_kernel<KV, D, P, M>, 64, 0) != hipSuccess ||
+            n <= 0)
+            n = 8;
         waves_per_cu = n;
     }
 #ifdef PKV_MAX_WAVES_PER_CU
     waves_per_cu = waves_per_cu < PKV_MAX_WAVES_PER_CU ? waves_per_cu : PKV_MAX_WAVES_PER_CU;
 #endif
-    int nwt = waves_per_cu * device_cus();
-    nwt = nwt < kMaxWaves ? nwt : kMaxWaves;
-    hipLaunchKernelGGL(kern, dim3(nwt), dim3(64), 0, stream, a);
+    const int nwt = waves_per_cu * device_cus();
+    return nwt < kMaxWaves ? nwt : kMaxWaves;
+}
+
+template <int KV, int D, int M>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+    constexpr int P = Depth<KV, D>::P;
+    hipLaunchKernelGGL((paged_decode_kernel<KV, D, P, M>), dim3(waves_t<KV, D, M>()), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1525,11 +1534,70 @@ hipError_t launch_prefill(int cache_dtype, int head_dim, const DecodeArgs& a, in
     return hipErrorInvalidValue;
 }
 
+int decode_waves(int cache_dtype, int head_dim) {
+    if (cache_dtype == kF32 && head_dim == 64) return waves_t<kF32, 64, kModePlain>();
+    if (cache_dtype == kF32 && head_dim == 128) return waves_t<kF32, 128, kModePlain>();
+    if (cache_dtype == kBF16 && head_dim == 64) return waves_t<kBF16, 64, kModePlain>();
+    if (cache_dtype == kBF16 && head_dim == 128) return waves_t<kBF16, 128, kModePlain>();
+    if (cache_dtype == kFP8 && head_dim == 64) return waves_t<kFP8, 64, kModePlain>();
+    if (cache_dtype == kFP8 && head_dim == 128) return waves_t<kFP8, 128, kModePlain>();
+    return kMaxWaves;
+}
+
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
     if (a.cu_q) return launch_c<kModeMulti>(cache_dtype, head_dim, a, stream);
     if (a.prefix_leader) return launch_c<kModeShared>(cache_dtype, head_dim, a, stream);
     return launch_c<kModePlain>(cache_dtype, head_dim, a, stream);
+}
+
+}  // namespace pkv
+
+// ---- static scratch of the no-allocation decode ----
+//
+// paged_attention_decode_noalloc runs the plain decode with its workspace
+// (arrival counters, then the partial-state slots of the waves) in this
+// file-scope device array instead of a caller's buffer.  Every GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends.  In host code `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to a kernel.
+namespace pkv {
+namespace {
+
+__device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t noalloc_scratch(float** out, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return hipErrorInvalidSymbol;
+        // The counters must start at zero (every call that completes leaves them so): cleared once, by a
+        // fill kernel on the first call's stream, ahead of that call's decode.
+        hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+                           int64_t(kSlotBase));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
 }
 
 }  // namespace pkv

@@ -129,6 +129,16 @@ inline int64_t state_row_floats(int head_dim) { return int64_t(head_dim) + 4; }
 
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
+// Persistent waves a plain decode launch runs for this pool type and head_dim
+// (its partial-state slots are 2 per wave).
+int decode_waves(int cache_dtype, int head_dim);
+
+// The no-allocation decode's static scratch: its size, and its device address
+// on the current device (taken, and its counters cleared on `stream`, by the
+// first call on each device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;  // PKV_NOALLOC_SCRATCH_BYTES
+hipError_t noalloc_scratch(float** out, hipStream_t stream);
+
 // Query columns of one prefill wave: floor(kPrefillWaveCols / G) new tokens
 // times the G query heads of one KV head (G at most kPrefillWaveCols; columns
 // past the last whole token stay empty).

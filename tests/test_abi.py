@@ -40,14 +40,14 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 8
+    assert lib.pkv_abi_version() == 9
     # the header's version history names every version up to the current one
     text = open(HEADER).read()
     hist = text[text.index("Version of this ABI"):text.index("int pkv_abi_version(void);")]
     for v in range(2, lib.pkv_abi_version() + 1):
         assert re.search(rf"\b{v} = ", hist), f"ABI history in pkv.h does not name version {v}"
     assert not re.search(rf"\b{lib.pkv_abi_version() + 1} = ", hist), "ABI history names a version past the library's"
-    for st in range(7):
+    for st in range(8):
         assert lib.pkv_status_string(st)
     assert lib.pkv_status_string(99) == b"unknown status"
 
@@ -107,6 +107,29 @@ def test_decode_validation(lib):
     assert _dec(lib, ws=0, wsb=0) == WORKSPACE
     assert _dec(lib, wsb=need - 1) == WORKSPACE
     assert _dec(lib, B=0) == OK                        # empty batch: no launch
+
+
+def _dec_noalloc(lib, **kw):
+    a = dict(out=A, q=A, qd=1, kc=A, vc=A, cd=1, bt=A, MB=64, cl=A, B=4, H=32, Hkv=8, D=128, bs=16, NB=300,
+             scale=0.088, ks=1.0, vs=1.0, part=0)
+    a.update(kw)
+    return lib.paged_attention_decode_noalloc(a["out"], a["q"], a["qd"], a["kc"], a["vc"], a["cd"], a["bt"], a["MB"],
+                                              a["cl"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                              a["scale"], a["ks"], a["vs"], a["part"], None)
+
+
+def test_noalloc_decode_validation(lib):
+    """The no-allocation decode validates like the decode, before it touches its scratch or the device."""
+    assert _dec_noalloc(lib, B=-1) == INVALID
+    assert _dec_noalloc(lib, H=30) == INVALID
+    assert _dec_noalloc(lib, part=20) == INVALID
+    assert _dec_noalloc(lib, D=256) == UNSUPPORTED
+    assert _dec_noalloc(lib, qd=0, cd=1) == UNSUPPORTED
+    assert _dec_noalloc(lib, B=1 << 20, MB=4096) == UNSUPPORTED
+    assert _dec_noalloc(lib, q=A + 4) == ALIGN
+    assert _dec_noalloc(lib, out=0) == INVALID
+    assert _dec_noalloc(lib, B=0) == OK                 # empty batch: no launch, no scratch
+    assert b"scratch" in lib.pkv_status_string(7)
 
 
 def _ws(run_heads, d):
