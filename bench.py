@@ -156,8 +156,9 @@ def prefill_read_bytes(w) -> int:
 
 
 def kernel_key(args) -> str:
-    """The kernel a counter summary covers: the prefill's for --prefill, else the decode's."""
-    return "paged_prefill_kernel" if args.prefill else "paged_decode_kernel"
+    """The kernel a counter summary covers (a substring of its name): the prefill's for --prefill (bf16/fp8
+    pools run paged_prefill32_kernel, f32 pools paged_prefill_kernel), else the decode's."""
+    return "paged_prefill" if args.prefill else "paged_decode_kernel"
 
 
 def profile_key(args) -> str:

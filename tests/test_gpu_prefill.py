@@ -68,23 +68,25 @@ def test_prefill_parity(gpu, hq, hkv, d, cache, pat):
     assert np.array_equal(got, wide)
 
 
-def test_prefill_rows_and_bound(gpu):
-    """Rows no sequence claims are not written; tokens at or past max_q_len are not computed."""
+@pytest.mark.parametrize("bound", [32, 27, 5])
+def test_prefill_rows_and_bound(gpu, bound):
+    """Rows no sequence claims are not written; tokens at or past max_q_len are not computed, also when the
+    bound is not a multiple of a wave's or a workgroup's tokens."""
     lens, nnew = [90, 300, 40], [20, 70, 10]
     w = W.make_multi("prefill_rows", 5, lens, nnew, 32, 8, 128, "bf16", "bf16")
     kp, vp = _gpu.gpu_pools(w, w.layout)
     ok, ov = _gpu.oracle_pools(w, w.layout)
     want = _gpu.oracle_varlen(w, w.layout, ok, ov)
     q = _gpu.to_dev(w.q, "bf16")
-    _gpu.note("prefill max_q_len below a sequence's count")
+    _gpu.note(f"prefill max_q_len {bound} below a sequence's count")
     out = torch.full_like(q, float("nan"))
-    _prefill(w, kp, vp, max_q=32, out=out)
+    _prefill(w, kp, vp, max_q=bound, out=out)
     o = _gpu.widen(_gpu.to_host(out, "bf16"), "bf16")
     cu = w.cu_q
     for s, n in enumerate(nnew):
         rows = np.arange(cu[s], cu[s + 1])
-        done = rows[:min(n, 32)]
-        skipped = rows[min(n, 32):]
+        done = rows[:min(n, bound)]
+        skipped = rows[min(n, bound):]
         assert np.max(np.abs(o[done] - want[done])) <= _gpu.TOL["bf16"]
         assert np.all(np.isnan(o[skipped]))
     _gpu.note("prefill unclaimed rows")
