@@ -1812,13 +1812,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 2 
 #define PKV_PF_WAVES 4
 #endif
 #ifndef PKV_PF_SUB
-#define PKV_PF_SUB 1
+#define PKV_PF_SUB 2
 #endif
 constexpr int kPfWaves = PKV_PF_WAVES;  // waves per workgroup
 constexpr int kPfSub = PKV_PF_SUB;      // 32-token steps per LDS stage (one barrier per stage)
 
 template <int KV, int D>
-__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_lds_kernel(
+#ifndef PKV_PF_OCC
+#define PKV_PF_OCC 2
+#endif
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(PKV_PF_OCC))) void paged_prefill_lds_kernel(
     DecodeArgs a) {
     constexpr int ELT = KV == kBF16 ? 2 : 1;
     constexpr int TILE = kBlockTokens * D * ELT;  // one block of one KV head, bytes
@@ -1919,25 +1922,31 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             ent[b] = nxt[b];
             nxt[b] = table_entry(NB * (sg + 2) + b);
         }
+        // scores S^T = K Q^T of every step of the stage first (K operands from LDS), so that the matrix
+        // cores work on the later steps' scores while the earlier steps' softmax runs
+        f32x16 saccs[kPfSub];
+#pragma unroll
+        for (int sb = 0; sb < kPfSub; ++sb) {
+            const uint8_t* kt = &lds[buf][2 * sb * TILE] + (n < 16 ? 0 : TILE);
+            saccs[sb] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                bf16x8 kop;
+                if constexpr (KV == kBF16)
+                    kop = __builtin_bit_cast(bf16x8,
+                                             *reinterpret_cast<const uint4*>(kt + ((2 * i + h) * kBlockTokens + ktok) * 16));
+                else
+                    kop = widen8<KV>(*reinterpret_cast<const uint2*>(kt + (i * kBlockTokens + ktok) * 16 + 8 * h));
+                saccs[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[i], saccs[sb], 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int sb = 0; sb < kPfSub; ++sb) {
         const int st = kPfSub * sg + sb;
         const int nv0 = vt[2 * sb], nv1 = vt[2 * sb + 1];
-        const uint8_t* kl = &lds[buf][2 * sb * TILE];
         const uint8_t* vl = &lds[buf][(NB + 2 * sb) * TILE];
         const int k0 = 32 * st;
-        // scores S^T = K Q^T, K operands from LDS
-        f32x16 sacc = f32x16{};
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const uint8_t* kt = kl + (n < 16 ? 0 : TILE);
-            bf16x8 kop;
-            if constexpr (KV == kBF16)
-                kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + ((2 * i + h) * kBlockTokens + ktok) * 16));
-            else
-                kop = widen8<KV>(*reinterpret_cast<const uint2*>(kt + (i * kBlockTokens + ktok) * 16 + 8 * h));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[i], sacc, 0, 0, 0);
-        }
+        f32x16& sacc = saccs[sb];
         // V operands of this step (masked below when tokens are absent)
         KOp vv[NT][2];
 #pragma unroll
