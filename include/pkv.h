@@ -88,7 +88,10 @@ typedef enum pkv_status {
  *   6 = paged_attention_varlen;
  *   7 = the block manager's prefix caching;
  *   8 = paged_attention_prefill;
- *   9 = paged_attention_decode_noalloc and PKV_ERR_SCRATCH. */
+ *   9 = paged_attention_decode_noalloc and PKV_ERR_SCRATCH;
+ *  10 = the shared-prefix decode merges prefix and suffix states in a second
+ *       launch: the workspace loses its meeting counters (every workspace is
+ *       1 MiB smaller) and the num_seqs * runs limit of the cascade is gone. */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -210,11 +213,11 @@ int paged_attention_decode(void* out,
  * Arguments, results and errors as paged_attention_decode (same kernel, same
  * result bits), plus PKV_ERR_SCRATCH, returned before anything is launched,
  * when the states of the persistent waves do not fit: the counters (about
- * 1.1 MB) plus two states of 32 + run_heads * head_dim floats per wave, with
+ * 64 KB) plus two states of 32 + run_heads * head_dim floats per wave, with
  * run_heads the largest divisor of num_heads / num_kv_heads that is at most
  * 16 and 2048 waves on MI355X for 16-bit and 8-bit pools.  So every shape
- * with run_heads <= 8 fits at head_dim 128 (18 MB at 8), and run_heads 16 at
- * head_dim 128 does not (35 MB).
+ * with run_heads <= 8 fits at head_dim 128 (17.4 MB at 8), and run_heads 16
+ * at head_dim 128 does not (34.1 MB).
  * Every call on one GPU shares that GPU's array: calls that overlap on one
  * GPU (on different streams without ordering between them, or from several
  * threads) race and give unspecified results.  Calls on one stream are
@@ -236,11 +239,10 @@ int paged_attention_decode_noalloc(void* out,
  * paged_attention_cascade_workspace_bytes -- workspace size for
  * paged_attention_decode_cascade: the decode workspace with merge slots wide
  * enough for a prefix run's columns, then two arrays of num_seqs * num_heads
- * state rows of head_dim + 4 floats.  Grows with num_seqs.  The arrival
- * counters of the prefix/suffix meeting live in the region every workspace
- * reserves for counters, so one zero-filled buffer may serve plain and
- * cascade calls of any shape in turn.  Returns 0 for arguments
- * paged_attention_decode would reject.
+ * state rows of head_dim + 4 floats.  Grows with num_seqs.  The state rows
+ * hold data only; the counters sit where every workspace keeps them, so one
+ * zero-filled buffer may serve plain and cascade calls of any shape in turn.
+ * Returns 0 for arguments paged_attention_decode would reject.
  */
 size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
@@ -270,8 +272,12 @@ size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_hea
  * consecutive sequences (4 for a GQA group of 4, 16 for one query head per KV
  * head): one prefix run per chunk and KV head reads the shared blocks through
  * the chunk's first table row and scores them for all the chunk's heads at
- * once.  Each sequence's remaining blocks are read by its own runs, and the
- * two softmax states of every head are merged (same rule as partitions).
+ * once.  Each sequence's remaining blocks are read by its own runs.  Both
+ * kinds of run store their finished softmax state per (sequence, head) in the
+ * workspace's state rows, and a second, small launch on the same stream merges
+ * the two states of every head whose sequence has both (same rule as
+ * partitions) and writes its output; a head whose context ends inside the
+ * shared blocks is written by its prefix run directly.
  * A sequence whose entries disagree with its chunk's first sequence (another
  * leader or shared length, a leader after it) is decoded on its own; results
  * are unspecified (but memory-safe) when the shared blocks are in fact not the
@@ -280,9 +286,7 @@ size_t paged_attention_cascade_workspace_bytes(int32_t num_seqs, int32_t num_hea
  *                the same zero-fill and reuse contract as for
  *                paged_attention_decode.
  * Errors: as paged_attention_decode (PKV_ERR_UNSUPPORTED also when the state
- * rows need 2^31 bytes or more, or num_seqs * runs > 2^18, runs =
- * num_heads / query heads per run); PKV_ERR_INVALID_ARG for NULL prefix
- * arrays.
+ * rows need 2^31 bytes or more); PKV_ERR_INVALID_ARG for NULL prefix arrays.
  */
 int paged_attention_decode_cascade(void* out,
                                    const void* q, int q_dtype,

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -126,7 +126,7 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
     if (groups * runs * max_blocks_per_seq * (cascade ? 2 : 1) >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
     if (multi && int64_t(num_q_rows) * num_heads * head_dim >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
     const int64_t state_bytes = int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim) * 4;
-    if (cascade && (state_bytes >= (int64_t(1) << 31) || int64_t(num_seqs) * runs > pkv::kMeetCounters))
+    if (cascade && state_bytes >= (int64_t(1) << 31))
         return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
@@ -188,7 +188,6 @@ int decode_impl(void* out, const void* q, int q_dtype, const void* k_cache, cons
         a.prefix_leader = prefix_leader;
         a.prefix_blocks = prefix_blocks;
         a.members = members;
-        a.meet = reinterpret_cast<int32_t*>(a.ws + pkv::kMeetBase);
         a.pstate = a.ws + base;
         a.sstate = a.pstate + pkv::align_floats(int64_t(num_seqs) * num_heads * pkv::state_row_floats(head_dim));
         a.state_bytes = int32_t(state_bytes);

@@ -864,67 +864,21 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
     return true;
 }
 
-// merge(prefix, suffix) for the meeting: the same rule as state_merge with
-// every product and sum rounded on its own (no fused multiply-add), so the
-// two places that compute it produce the same bits whichever side came last.
-template <int NVC>
-__device__ __forceinline__ void meet_merge(State<NVC>& p, const State<NVC>& t) {
-#pragma clang fp contract(off)
-    const float M = fmaxf(p.m, t.m);
-    const float wp = p.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(p.m - M);
-    const float wt = t.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(t.m - M);
-    p.m = M;
-    p.l = p.l * wp + t.l * wt;
-#pragma unroll
-    for (int c = 0; c < NVC; ++c) p.acc[c] = p.acc[c] * wp + t.acc[c] * wt;
-}
-
-// Shared-prefix meeting.  The output of a covered (sequence, head) row is
-// merge(prefix state, suffix state).  Each side stores its rows, then counts
-// itself in the (sequence, run) counter; the second arrival resets it, loads
-// the other side's rows and writes the output.  Both sides merge as
-// merge(prefix, suffix), so the result does not depend on which came second.
+// Shared-prefix decode: the finished state of a covered (sequence, head) row
+// from its prefix run and from its own (suffix) runs are both stored as state
+// rows; cascade_merge_kernel, launched after the decode on the same stream,
+// combines them with the merge rule and writes the output.  Rows whose
+// sequence has no suffix runs (its context ends inside the shared blocks) are
+// written straight from the prefix run; uncovered sequences are plain runs.
 template <int QT, int D, int NVC>
-__device__ void meet_suffix(const DecodeArgs& a, int s, int hg, const Cols& cm, const State<NVC>& st) {
+__device__ void finish_suffix(const DecodeArgs& a, const Cols& cm, const State<NVC>& st) {
     row_store<D>(a.sstate, a.state_bytes, cm.row, st, cm.hv);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // the rows have reached the coherent level before they are counted
-    int* ctr = a.meet + int64_t(s) * a.runs + hg;
-    int old = 0;
-    if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old == 0) return;  // the prefix rows come later
-    if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    State<NVC> p;
-    row_load<D>(a.pstate, a.state_bytes, cm.row, p, cm.hv);
-    meet_merge(p, st);
-    state_output<QT, D>(a, cm.row, p, cm.hv);
 }
 
 template <int QT, int D, int NVC>
-__device__ void meet_prefix(const DecodeArgs& a, int s, int hg, const Cols& cm, State<NVC>& st) {
-    const int lane = lane_id(), col = lane & 15, g = lane >> 4;
-    const int member = col / a.rh;
-    const bool meet = cm.hv && cm.sne;  // rows whose sequence has suffix runs
-    row_store<D>(a.pstate, a.state_bytes, cm.row, st, meet);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    int old = 0;  // one arrival per member sequence, by its first column's lane of row group 0
-    if (g == 0 && meet && col == member * a.rh) {
-        int* ctr = a.meet + int64_t(s + member) * a.runs + hg;
-        old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    old = __shfl(old, member * a.rh);
-    const bool merge = meet && old == 1;    // the suffix rows are there
-    const bool direct = cm.hv && !cm.sne;   // no suffix: the prefix state is the whole state
-    if (!__ballot(merge || direct)) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    State<NVC> t;
-    row_load<D>(a.sstate, a.state_bytes, cm.row, t, merge);
-    if (merge) meet_merge(st, t);
-    state_output<QT, D>(a, cm.row, st, merge || direct);
+__device__ void finish_prefix(const DecodeArgs& a, const Cols& cm, const State<NVC>& st) {
+    row_store<D>(a.pstate, a.state_bytes, cm.row, st, cm.hv && cm.sne);  // rows whose sequence has suffix runs
+    state_output<QT, D>(a, cm.row, st, cm.hv && !cm.sne);               // the rest: the prefix state is whole
 }
 
 constexpr int kLenChunks = 8;  // 64-sequence chunks of lengths read per round trip
@@ -1278,9 +1232,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 if (whole) {
                     if constexpr (M == kModeShared) {
                         if (piece_kind(sl[0]) == 1)
-                            meet_prefix<QT, D>(a, sl[0].s, piece_hg(sl[0]), cm, st);
+                            finish_prefix<QT, D>(a, cm, st);
                         else if (piece_kind(sl[0]) == 2)
-                            meet_suffix<QT, D>(a, sl[0].s, piece_hg(sl[0]), cm, st);
+                            finish_suffix<QT, D>(a, cm, st);
                         else
                             state_output<QT, D>(a, cm.row, st, cm.hv);
                     } else {
@@ -2068,6 +2022,46 @@ hipError_t launch_prefill_t(const DecodeArgs& a, int items, hipStream_t stream) 
 
 }  // namespace
 
+// ---- shared-prefix decode, second pass: merge(prefix, suffix) of every covered row with suffix runs ----
+//
+// 32 threads per (sequence, head) row, each taking D / 32 consecutive dimensions.  A row's two states
+// (m, l, acc) combine as M = max(m_p, m_s), out = v_scale * (2^(m_p - M) acc_p + 2^(m_s - M) acc_s) /
+// (2^(m_p - M) l_p + 2^(m_s - M) l_s), a side without scores (m = -inf) weighing 0.  Which rows are covered
+// is decided from the sharing arrays exactly as in the decode (seq_info), so each row is written once.
+constexpr int kMergeRows = 8;  // rows per 256-thread workgroup
+
+template <int QT, int D>
+__global__ __launch_bounds__(32 * kMergeRows) void cascade_merge_kernel(DecodeArgs a) {
+    constexpr int E = D / 32;  // dimensions per thread
+    const int64_t row = int64_t(blockIdx.x) * kMergeRows + threadIdx.x / 32;
+    const int t = threadIdx.x % 32;
+    if (row >= int64_t(a.num_seqs) * a.num_heads) return;
+    const int s = int(row / a.num_heads);
+    const SeqInfo si = seq_info<kModeShared>(a, s);
+    const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
+    if (si.cl < 0 || nb <= si.pbe) return;  // not covered, or no suffix runs: written by the decode
+    const float* pr = a.pstate + row * (D + 4);
+    const float* sr = a.sstate + row * (D + 4);
+    const float mp = pr[D], lp = pr[D + 1], ms = sr[D], ls = sr[D + 1];
+    const float M = fmaxf(mp, ms);
+    const float wp = mp == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
+    const float ws = ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+    const float l = lp * wp + ls * ws;
+    const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = (pr[E * t + e] * wp + sr[E * t + e] * ws) * inv;
+    if constexpr (QT == kF32) {
+        float* out = static_cast<float*>(a.out) + row * D + E * t;
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = o[e];
+    } else {
+        uint16_t* out = static_cast<uint16_t*>(a.out) + row * D + E * t;
+#pragma unroll
+        for (int e = 0; e < E; e += 2) *reinterpret_cast<uint32_t*>(out + e) = pack_bf16(o[e], o[e + 1]);
+    }
+}
+
 template <int M>
 hipError_t launch_c(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
     if (cache_dtype == kF32 && head_dim == 64) return launch_t<kF32, 64, M>(a, stream);
@@ -2103,7 +2097,17 @@ int decode_waves(int cache_dtype, int head_dim) {
 hipError_t launch_decode(int cache_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
     if (a.cu_q) return launch_c<kModeMulti>(cache_dtype, head_dim, a, stream);
-    if (a.prefix_leader) return launch_c<kModeShared>(cache_dtype, head_dim, a, stream);
+    if (a.prefix_leader) {
+        const hipError_t e = launch_c<kModeShared>(cache_dtype, head_dim, a, stream);
+        if (e != hipSuccess) return e;
+        const int64_t rows = int64_t(a.num_seqs) * a.num_heads;
+        const dim3 grid(uint32_t((rows + kMergeRows - 1) / kMergeRows));
+        if (cache_dtype == kF32 && head_dim == 64) hipLaunchKernelGGL((cascade_merge_kernel<kF32, 64>), grid, dim3(256), 0, stream, a);
+        else if (cache_dtype == kF32) hipLaunchKernelGGL((cascade_merge_kernel<kF32, 128>), grid, dim3(256), 0, stream, a);
+        else if (head_dim == 64) hipLaunchKernelGGL((cascade_merge_kernel<kBF16, 64>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((cascade_merge_kernel<kBF16, 128>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     return launch_c<kModePlain>(cache_dtype, head_dim, a, stream);
 }
 

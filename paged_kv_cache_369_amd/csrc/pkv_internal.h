@@ -62,8 +62,6 @@ inline int run_heads(int group) {
 // completes leaves its counters at zero again):
 //   kWsHeader reserved words;
 //   kMergeLevels x kMaxWaves int32 arrival counters (one per merge group);
-//   kMeetCounters int32 arrival counters of the shared-prefix meeting (one per
-//   (sequence, run); zero and unused in plain decode);
 //   two partial-state slots per wave: slot 0 for the run the wave continues
 //   from the wave before it, slot 1 for the run it hands on to the waves
 //   after it.  Slot layout (floats): m[16], l[16], acc[columns][D].
@@ -73,10 +71,8 @@ inline int run_heads(int group) {
 constexpr int kWsHeader = 16;
 constexpr int kMergeFanIn = 8;   // states one merge step combines
 constexpr int kMergeLevels = 4;  // kMergeFanIn^kMergeLevels >= kMaxWaves
-constexpr int kMeetCounters = 1 << 18;
 constexpr int kSlotHead = 2 * kMaxRunHeads;
-constexpr int64_t kMeetBase = kWsHeader + int64_t(kMergeLevels) * kMaxWaves;
-constexpr int64_t kSlotBase = kMeetBase + kMeetCounters;
+constexpr int64_t kSlotBase = kWsHeader + int64_t(kMergeLevels) * kMaxWaves;
 inline int64_t slot_floats(int columns, int head_dim) { return kSlotHead + int64_t(columns) * head_dim; }
 inline int64_t workspace_floats(int columns, int head_dim) {
     return kSlotBase + 2 * int64_t(kMaxWaves) * slot_floats(columns, head_dim);
@@ -105,7 +101,6 @@ struct DecodeArgs {
     // shared-prefix decode only (null / 0 otherwise)
     const int32_t* prefix_leader;  // [num_seqs] first sequence of each sequence's sharing group
     const int32_t* prefix_blocks;  // [num_seqs] leading blocks shared with that group
-    int32_t* meet;                 // [num_seqs * runs] arrival counters of prefix and suffix states (workspace)
     float* pstate;                 // [num_seqs * num_heads] state rows of the prefix part
     float* sstate;                 // [num_seqs * num_heads] state rows of the suffix part
     int32_t members;               // sequences (shared prefix) or new tokens (several queries) per run's columns

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 9
+    assert lib.pkv_abi_version() == 10
     # the header's version history names every version up to the current one
     text = open(HEADER).read()
     hist = text[text.index("Version of this ABI"):text.index("int pkv_abi_version(void);")]
@@ -133,9 +133,9 @@ def test_noalloc_decode_validation(lib):
 
 
 def _ws(run_heads, d):
-    """Header (16 words) + 4 merge levels x 4096 arrival counters + 2^18 shared-prefix meeting counters + two
-    partial-state slots per persistent wave (4096 at most) of 32 + run_heads * D floats."""
-    return (16 + 4 * W + (1 << 18) + 2 * W * (32 + run_heads * d)) * 4
+    """Header (16 words) + 4 merge levels x 4096 arrival counters + two partial-state slots per persistent
+    wave (4096 at most) of 32 + run_heads * D floats."""
+    return (16 + 4 * W + 2 * W * (32 + run_heads * d)) * 4
 
 
 def _cws(b, hq, columns, d):
@@ -203,7 +203,9 @@ def test_cascade_validation_and_workspace(lib):
     assert _cas(lib, pl=A + 2) == ALIGN
     assert _cas(lib, B=-1) == INVALID
     assert _cas(lib, D=96) == UNSUPPORTED
-    assert _cas(lib, B=(1 << 18) // 8 + 1, MB=4) == UNSUPPORTED       # more (sequence, run) pairs than counters
+    assert _cas(lib, B=130000, MB=4) == UNSUPPORTED                    # state rows of 2^31 bytes or more
+    big = (1 << 18) // 8 + 1                                           # (sequence, run) pairs are not limited:
+    assert _cas(lib, B=big, MB=4, wsb=cws(big, 32, 8, 128, 4, 16, 0) - 1) == WORKSPACE  # only the workspace
     need = cws(4, 32, 8, 128, 64, 16, 0)
     assert _cas(lib, wsb=need - 1) == WORKSPACE
     assert _cas(lib, wsb=lib.paged_attention_workspace_bytes(4, 32, 8, 128, 64, 16, 0)) == WORKSPACE

@@ -18,7 +18,7 @@ from tests import _gpu
 
 pytestmark = pytest.mark.gpu
 
-COUNTERS = (0, (16 + 4 * 4096 + (1 << 18)) * 4)  # byte range of every counter in a workspace (header included)
+COUNTERS = (0, (16 + 4 * 4096) * 4)  # byte range of every counter in a workspace (header included)
 
 # groups of (prefix tokens, member lengths): block-aligned and ragged prefixes, members with no private
 # token, a member-less-than-a-chunk group, a group of 19 (ragged last chunk), an unshared sequence
@@ -137,7 +137,7 @@ def test_workspace_shared_with_plain_calls(gpu):
 
 def test_long_shared_prefix_merge_tree(gpu):
     """A 40000-token prefix shared by 6 samples beside short sequences: the prefix runs are cut over hundreds
-    of waves (tree merge), then meet their samples' suffix runs."""
+    of waves (tree merge), then are merged with their samples' suffix states."""
     groups = [(40000, [40000 + 7 * i + 1 for i in range(6)]), (0, [5]), (3000, [3001, 3100]), (0, [1])]
     w = W.make_shared("casclong", 33, groups, 32, 8, 128, "bf16", "bf16")
     _gpu.note("cascade long prefix")

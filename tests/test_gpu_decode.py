@@ -300,7 +300,7 @@ def test_long_context_merge_tree(gpu, hq, hkv, d, cache, part):
         torch.cuda.synchronize()
         outs.append(_gpu.widen(_gpu.to_host(out, w.q_dtype), w.q_dtype))
     assert np.array_equal(outs[0], outs[1])
-    counters = ws[:(16 + 4 * 4096 + (1 << 18)) * 4].view(torch.int32)  # header words, merge and meeting counters
+    counters = ws[:(16 + 4 * 4096) * 4].view(torch.int32)  # header words and merge counters
     assert int(torch.count_nonzero(counters)) == 0
     ok, ov = _gpu.oracle_pools(w, w.layout)
     want = _gpu.oracle_decode(w, w.layout, ok, ov)

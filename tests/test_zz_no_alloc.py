@@ -64,7 +64,7 @@ def test_noalloc_sixteen_heads_per_run_at_head_dim_64(gpu):
 
 
 def test_noalloc_refuses_states_beyond_the_scratch(gpu):
-    """16 query heads per KV head at head_dim 128 need 35 MB of states: refused, nothing launched or written."""
+    """16 query heads per KV head at head_dim 128 need 34 MB of states: refused, nothing launched or written."""
     w = W.make_custom("noalloc_big", 77, [100, 40], 16, 1, 128, "bf16", "bf16")
     kp, vp = _gpu.gpu_pools(w, w.layout)
     q = _gpu.to_dev(w.q, "bf16")
