@@ -568,6 +568,34 @@ __device__ __forceinline__ void load_tile(const DecodeArgs& a, int kvh, int id, 
     for (int c = 0; c < GE::NVC; ++c) t.v[c] = load_as<VLoad<KV>, NT>(vt + c * 16 * kBlockTokens * GE::ELT);
 }
 
+// Combine x over the four lanes of this lane's column (lanes lane % 16 + 16 r):
+// the gfx950 row swaps exchange rows 0<->1 and 2<->3 of 16 lanes, then the
+// two halves of 32 lanes, in the vector ALU (no trip through the LDS
+// crossbar).  The second operand of each swap goes through an opaque copy so
+// that the compiler cannot merge the two operands of the swap into one value.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t x) {
+    uint32_t y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
+__device__ __forceinline__ float column_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), opaque_copy(__float_as_uint(m)), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// The sum over the column as (r0 + r1) + (r2 + r3), the same in every lane.
+__device__ __forceinline__ float column_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+    const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), opaque_copy(__float_as_uint(m)), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Running softmax state of one run inside the streaming loop, in the
 // matrix-core output layout (see State); lsum is this lane's share of the
 // normaliser (its four rows), summed over the row groups when the state closes.
@@ -587,10 +615,8 @@ __device__ __forceinline__ void run_reset(Run<NVC>& r) {
 
 template <int NVC>
 __device__ __forceinline__ void run_close(const Run<NVC>& r, State<NVC>& st) {
-    float lt = r.lsum + __shfl_xor(r.lsum, 16);
-    lt += __shfl_xor(lt, 32);
     st.m = r.m;
-    st.l = lt;
+    st.l = column_sum(r.lsum);
 #pragma unroll
     for (int c = 0; c < NVC; ++c) st.acc[c] = r.acc[c];
 }
@@ -649,9 +675,7 @@ __device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV
         bm[c] = fmaxf(fmaxf(sv[c][0], sv[c][1]), fmaxf(sv[c][2], sv[c][3]));
     }
 #pragma unroll
-    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 16));
-#pragma unroll
-    for (int c = 0; c < CT; ++c) bm[c] = fmaxf(bm[c], __shfl_xor(bm[c], 32));
+    for (int c = 0; c < CT; ++c) bm[c] = column_max(bm[c]);
     float alpha[CT], pw[CT][4];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -690,31 +714,46 @@ __device__ __forceinline__ void consume_tiles(const DecodeArgs& a, const Tile<KV
         }
     } else {
         i16x4 pb[CT];
+        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const uint32_t p01 = pack_bf16(pw[c][0], pw[c][1]);
             const uint32_t p23 = pack_bf16(pw[c][2], pw[c][3]);
-            rs[c].lsum = rs[c].lsum * alpha[c] + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                                                  (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+            // the normaliser sums the rounded weights the value product uses
+            rs[c].lsum = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, p23), ones,
+                __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01), ones, rs[c].lsum * alpha[c], false),
+                false);
             pb[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
         }
-        const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
-        const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
+        // V entries of tokens past the block's valid ones are zeroed (their
+        // weights are 0, but the memory may hold any bits); a full block,
+        // the usual case, needs no mask
+        auto pv = [&](auto masked) {
+            const uint32_t mlo = cnt >= 2 ? 0xffffffffu : (cnt == 1 ? 0x0000ffffu : 0u);
+            const uint32_t mhi = cnt >= 4 ? 0xffffffffu : (cnt == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
-        for (int v = 0; v < GE::NVC; ++v) {
-            uint2 vv;
-            if constexpr (KV == kBF16) {
-                vv = t.v[v];
-            } else {
-                vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[v]), fp8x2_to_bf16x2<true>(t.v[v]));
+            for (int v = 0; v < GE::NVC; ++v) {
+                uint2 vv;
+                if constexpr (KV == kBF16) {
+                    vv = t.v[v];
+                } else {
+                    vv = make_uint2(fp8x2_to_bf16x2<false>(t.v[v]), fp8x2_to_bf16x2<true>(t.v[v]));
+                }
+                if constexpr (decltype(masked)::value) {
+                    vv.x &= mlo;
+                    vv.y &= mhi;
+                }
+                const i16x4 va = __builtin_bit_cast(i16x4, vv);
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+                    rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[c], rs[c].acc[v], 0, 0, 0);
             }
-            vv.x &= mlo;
-            vv.y &= mhi;
-            const i16x4 va = __builtin_bit_cast(i16x4, vv);
-#pragma unroll
-            for (int c = 0; c < CT; ++c)
-                rs[c].acc[v] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[c], rs[c].acc[v], 0, 0, 0);
-        }
+        };
+        if (nv >= kBlockTokens)
+            pv(std::false_type{});
+        else
+            pv(std::true_type{});
     }
 }
 
@@ -902,6 +941,7 @@ struct Piece {
     uint32_t contrib; // a cut run's waves: w0 | (w1 << 13) | first_in_slot1 << 26
     uint32_t cols;    // bit c: column c holds a head; bit 16 + c: its sequence has suffix runs (prefix runs)
     int ids;          // lane l < p1 - p0: physical block of the piece's l-th block
+    int kvh;          // KV head of the piece's run
     int qrow0;        // several queries: query row of column 0's token
     int cpos0;        // several queries: column 0's token position + 1 - context length (<= 0)
 };
@@ -1084,6 +1124,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             pc.info = 0;
             pc.cols = 0;
             pc.ids = -1;
+            pc.kvh = 0;
             return;
         }
         const int s = cur.base + i;
@@ -1126,6 +1167,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
         pc.ids = lane < int(pe - u) ? a.block_table[int64_t(s) * a.max_blocks + j + lane] : -1;
+        pc.kvh = hg * a.rh / a.group;
         // advance the walker past the piece
         spos = pc.p1;
         j += int(pe - u);
@@ -1183,7 +1225,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             if (!real && pos < sl[k].p1) {
                 const int off = int(pos - sl[k].p0);
                 id = __builtin_amdgcn_readlane(sl[k].ids, off);
-                kvh = piece_hg(sl[k]) * a.rh / a.group;
+                kvh = sl[k].kvh;
                 lim = sl[k].lim0 - off * kBlockTokens;
                 shared = piece_kind(sl[k]) == 1;
                 real = true;
@@ -1490,13 +1532,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int swap_quads(int u) { return u ^ ((((u >> 2) ^ (u >> 3)) & 1) * 12); }
 
 // x of this lane combined with x of lane ^ 32 (the other half of the same
-// column).  (The gfx950 row swap of 32 lanes does this in the vector ALU, but
-// the compiler in use folds the swap's two results into one when both of its
-// operands are the same value, which broke this combine; the lane shuffle is
-// one instruction per call and there are two such calls per step.)
-__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// column), by the gfx950 swap of 32-lane halves (operands as in column_max).
+__device__ __forceinline__ float halves_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
-__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float halves_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int KV, int D>
 struct Step32 {                      // K and V operands of one step (two blocks), per lane
