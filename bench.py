@@ -156,9 +156,15 @@ def prefill_read_bytes(w) -> int:
 
 
 def kernel_key(args) -> str:
-    """The kernel a counter summary covers (a substring of its name): the prefill's for --prefill (bf16/fp8
-    pools run paged_prefill32_kernel, f32 pools paged_prefill_kernel), else the decode's."""
+    """The kernel an SQ counter summary covers (a substring of its name): the prefill's for --prefill (bf16/fp8
+    pools run paged_prefill_lds_kernel, f32 pools paged_prefill_kernel), else the decode's."""
     return "paged_prefill" if args.prefill else "paged_decode_kernel"
+
+
+def call_kernels(args) -> list:
+    """Every kernel one timed call launches (substrings of their names): the shared-prefix decode is the
+    decode kernel and then the merge of prefix and suffix states."""
+    return [kernel_key(args)] + (["cascade_merge_kernel"] if args.cascade else [])
 
 
 def profile_key(args) -> str:
@@ -441,7 +447,7 @@ def summarize_traffic(args) -> int:
     fetch = _per_kernel(args.dec_fetch, "FETCH_SIZE")
     write = _per_kernel(args.dec_write, "WRITE_SIZE")
     kernels = {}
-    for key in (kernel_key(args),):
+    for key in call_kernels(args):
         f_kib, w_kib = _pick(fetch, key), _pick(write, key)
         kernels[key] = {"fetch_kib": f_kib, "write_kib": w_kib,
                         "fetch_bytes": f_kib * 1024 * fscale, "write_bytes": w_kib * 1024 * wscale}
@@ -727,7 +733,7 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "paged_decode_kernel (the whole decode call)",
+                     "kernel": (" + ".join(call_kernels(args)) + " (the whole call)"),
                      "avg_us": dec_us,
                      "p10_us": float(np.percentile(t_dec, 10)), "p90_us": float(np.percentile(t_dec, 90)),
                      "algorithmic_bytes_per_call": kv_bytes},
