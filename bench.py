@@ -246,17 +246,29 @@ def _csv_rows(directory: str, suffix: str):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(directory: str, command: str) -> int:
-    """Markdown table of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv)."""
+def summarize_trace(directory: str, command: str, last: int = 0) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv); with last > 0, also the
+    mean duration of each kernel's last `last` dispatches (the timed steps, after the warm-up ones), from
+    kernel_trace.csv."""
     rows = _csv_rows(directory, "kernel_stats.csv")
+    short = lambda name: name.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
     print(f"Command: `{command}`\n")
     print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
     print("|---|---|---|---|---|---|")
     for r in rows:
-        name = r["Name"]
-        short = name.replace("void ", "").replace("pkv::(anonymous namespace)::", "").split("(")[0]
-        print(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+        print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
               f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} % |")
+    if last > 0:
+        per = {}
+        for r in sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+            per.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"\nMean of each kernel's last {last} dispatches (the timed steps):\n")
+        print("| kernel | dispatches | mean (us) |")
+        print("|---|---|---|")
+        for k, v in per.items():
+            if len(v) >= last and ("pkv" in k or "paged" in k):
+                print(f"| `{k}` | {last} | {float(np.mean(v[-last:])):.1f} |")
     return 0
 
 
@@ -543,7 +555,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default 10; 30 with --prefill, whose matrix-bound "
+                         "calls take about 20 back-to-back calls to reach their sustained speed)")
     ap.add_argument("--workload", default="gqa8b", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1 = the workload's setting (0 = balanced split only)")
@@ -564,6 +578,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode step, run a plain device copy of known size (counter scale)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a markdown summary of a rocprofv3 --stats run")
+    ap.add_argument("--last", type=int, default=0,
+                    help="with --summarize-trace: also the mean of each kernel's last N dispatches")
     ap.add_argument("--summarize-traffic", action="store_true", help="write profiles/ HBM traffic summary")
     ap.add_argument("--summarize-counters", action="store_true", help="write profiles/ SQ counter summary")
     ap.add_argument("--utilisation", action="store_true",
@@ -576,9 +592,11 @@ def main() -> int:
     ap.add_argument("--command", action="append", dest="commands", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.warmup is None:
+        args.warmup = 30 if args.prefill else 10
 
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace, " && ".join(args.commands))
+        return summarize_trace(args.summarize_trace, " && ".join(args.commands), args.last)
     if args.utilisation:
         return utilisation(args)
     if args.summarize_counters:
@@ -750,7 +768,7 @@ def main() -> int:
         tf = fl / (dec_us * 1e-6) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic, "traffic_source": traffic_src,
-                              "kernel": "paged_prefill_kernel (the whole prefill call)", "avg_us": dec_us,
+                              "kernel": ("paged_prefill_kernel" if w.cache_dtype == "f32" else "paged_prefill_lds_kernel") + " (the whole prefill call)", "avg_us": dec_us,
                               "algorithmic_flops_per_call": fl, "kv_read_bytes_bound": kv_bytes}
         log(f"prefill: {fl / 1e9:.1f} GFLOP per call -> {tf:.1f} TFLOP/s")
 
