@@ -931,6 +931,7 @@ enum PieceFlags : int {
     kClose = 4,     // the state ends with this piece
     kEndsPart = 8,  // ... and so does this wave's part of the run
     kLocal = 16,    // the whole run lies in this wave's stretch
+    kReread = 32,   // other runs of the call read the same tiles (ordinary loads, so the L2 keeps them)
 };
 
 struct Piece {
@@ -1142,6 +1143,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
         if (close) f |= kClose;
         if (close && (seg_end == run_end || seg_end == hi)) f |= kEndsPart;
         if (run_first >= lo && pe == run_end) f |= kLocal;
+        // the prefix runs of a sharing group, and the token groups of a sequence with several, read
+        // tiles that other runs read again
+        if (pre || (M == kModeMulti && nq > a.members)) f |= kReread;
         pc.p0 = spos;
         pc.p1 = spos + (pe - u);
         pc.s = s;
@@ -1227,14 +1231,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 id = __builtin_amdgcn_readlane(sl[k].ids, off);
                 kvh = sl[k].kvh;
                 lim = sl[k].lim0 - off * kBlockTokens;
-                shared = piece_kind(sl[k]) == 1;
+                shared = (piece_flags(sl[k]) & kReread) != 0;
                 real = true;
             }
         }
         const bool ok = real && id >= 0 && id < a.num_blocks;
         nv = ok ? min(kBlockTokens, lim) : 0;
         lraw = lim;
-        if (M == kModeShared && shared)
+        if (M != kModePlain && shared)
             load_tile<KV, D, false>(a, ok ? kvh : 0, ok ? id : 0, tb);
         else
             load_tile<KV, D, true>(a, ok ? kvh : 0, ok ? id : 0, tb);
