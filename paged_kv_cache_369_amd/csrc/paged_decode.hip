@@ -422,12 +422,15 @@ struct Cursor {
 };
 
 template <int M>
-__device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int base) {
-    const int s = base + lane_id();
+__device__ __forceinline__ void cursor_set(Cursor& c, const DecodeArgs& a, int base, const SeqInfo& si) {
     c.base = base;
-    c.si = seq_info<M>(a, s);
-    c.inc = wave_scan(seq_units<M>(a, c.si, s));
+    c.si = si;
+    c.inc = wave_scan(seq_units<M>(a, c.si, base + lane_id()));
     c.tot = __builtin_amdgcn_readlane(c.inc, 63);
+}
+template <int M>
+__device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int base) {
+    cursor_set<M>(c, a, base, seq_info<M>(a, base + lane_id()));
 }
 
 template <int M>
@@ -1000,12 +1003,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     uint32_t U = 0;
     uint64_t U64 = 0;  // the same total, without wrap-around
     uint32_t ctot[kLenChunks];
+    SeqInfo sfirst[kLenChunks];  // the first kLenChunks chunks' entries, kept for the cursor
 #pragma unroll
     for (int c = 0; c < kLenChunks; ++c) ctot[c] = 0;
     for (int base = 0; base < a.num_seqs; base += 64 * kLenChunks) {
         SeqInfo si[kLenChunks];
 #pragma unroll
         for (int c = 0; c < kLenChunks; ++c) si[c] = seq_info<M>(a, base + 64 * c + lane);
+        if (base == 0) {
+#pragma unroll
+            for (int c = 0; c < kLenChunks; ++c) sfirst[c] = si[c];
+        }
 #pragma unroll
         for (int c = 0; c < kLenChunks; ++c) {
             const int cb = base + 64 * c;
@@ -1048,7 +1056,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             }
         }
     }
-    cursor_load<M>(cur, a, 64 * chunk);
+    if (chunk < kLenChunks) {  // the chunk's entries are still in registers: no second round trip
+        SeqInfo x = sfirst[0];
+#pragma unroll
+        for (int c = 1; c < kLenChunks; ++c)
+            if (c == chunk) x = sfirst[c];
+        cursor_set<M>(cur, a, 64 * chunk, x);
+    } else {
+        cursor_load<M>(cur, a, 64 * chunk);
+    }
     int i = 0;
     // Runs of a sequence: npre prefix runs over blocks [0, pbe) (when it leads
     // a prefix group), then its runs over blocks [pbe, nb).
