@@ -1947,11 +1947,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(P
         // cores work on the later steps' scores while the earlier steps' softmax runs
         f32x16 saccs[kPfSub];
 #pragma unroll
-        for (int sb = 0; sb < kPfSub; ++sb) {
-            const uint8_t* kt = &lds[buf][2 * sb * TILE] + (n < 16 ? 0 : TILE);
-            saccs[sb] = f32x16{};
+        for (int sb = 0; sb < kPfSub; ++sb) saccs[sb] = f32x16{};
+        // the steps' products interleaved, so that consecutive matrix steps use different accumulators
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
+        for (int i = 0; i < NK; ++i) {
+#pragma unroll
+            for (int sb = 0; sb < kPfSub; ++sb) {
+                const uint8_t* kt = &lds[buf][2 * sb * TILE] + (n < 16 ? 0 : TILE);
                 bf16x8 kop;
                 if constexpr (KV == kBF16)
                     kop = __builtin_bit_cast(bf16x8,
@@ -2040,10 +2042,11 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(P
         const bf16x8 p0 = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
         const bf16x8 p1 = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8<KV>(vv[t][0]), p0, acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8<KV>(vv[t][1]), p1, acc[t], 0, 0, 0);
-        }
         }
     }
     const float lt = halves_sum(lsum);
