@@ -358,13 +358,16 @@ __device__ __forceinline__ SeqInfo seq_info(const DecodeArgs& a, int s) {
     if constexpr (M == kModeShared) {
         const int pbs = shared_blocks(a, s, r.len);
         const int ld = a.prefix_leader[s];
-        if (pbs > 0 && ld >= 0 && ld <= s) {
-            const int c = ld + (s - ld) / a.members * a.members;
-            const bool ok = c == s || (a.prefix_leader[c] == ld && shared_blocks(a, c, clamped_len(a, c)) == pbs);
-            if (ok) {
-                r.pbe = pbs;
-                r.cl = c;
-            }
+        const bool led = ld >= 0 && ld <= s;
+        const int c = led ? ld + (s - ld) / a.members * a.members : s;  // in [0, s]
+        // c's entries are read whatever s's say (c is a valid sequence), so that the two sets of reads are
+        // two round trips, not a chain of four
+        const int ldc = a.prefix_leader[c];
+        const int pbc = shared_blocks(a, c, clamped_len(a, c));
+        const bool ok = c == s || (ldc == ld && pbc == pbs);
+        if (pbs > 0 && led && ok) {
+            r.pbe = pbs;
+            r.cl = c;
         }
     }
     return r;
@@ -2107,12 +2110,22 @@ __global__ __launch_bounds__(32 * kMergeRows) void cascade_merge_kernel(DecodeAr
     const int t = threadIdx.x % 32;
     if (row >= int64_t(a.num_seqs) * a.num_heads) return;
     const int s = int(row / a.num_heads);
+    // the two rows are read before the sharing arrays are (both are in bounds for any row), so that
+    // their loads overlap the dependent reads that decide whether the row is merged at all
+    using VE = typename std::conditional<E == 4, float4, float2>::type;
+    const float* pr = a.pstate + row * (D + 4);
+    const float* sr = a.sstate + row * (D + 4);
+    const VE pv = *reinterpret_cast<const VE*>(pr + E * t);
+    const VE sv = *reinterpret_cast<const VE*>(sr + E * t);
+    const float2 pml = *reinterpret_cast<const float2*>(pr + D);
+    const float2 sml = *reinterpret_cast<const float2*>(sr + D);
     const SeqInfo si = seq_info<kModeShared>(a, s);
     const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
     if (si.cl < 0 || nb <= si.pbe) return;  // not covered, or no suffix runs: written by the decode
-    const float* pr = a.pstate + row * (D + 4);
-    const float* sr = a.sstate + row * (D + 4);
-    const float mp = pr[D], lp = pr[D + 1], ms = sr[D], ls = sr[D + 1];
+    const float mp = pml.x, lp = pml.y, ms = sml.x, ls = sml.y;
+    float pa[E], sa[E];
+    __builtin_memcpy(pa, &pv, sizeof(pa));
+    __builtin_memcpy(sa, &sv, sizeof(sa));
     const float M = fmaxf(mp, ms);
     const float wp = mp == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
     const float ws = ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
@@ -2120,7 +2133,7 @@ __global__ __launch_bounds__(32 * kMergeRows) void cascade_merge_kernel(DecodeAr
     const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
     float o[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = (pr[E * t + e] * wp + sr[E * t + e] * ws) * inv;
+    for (int e = 0; e < E; ++e) o[e] = (pa[e] * wp + sa[e] * ws) * inv;
     if constexpr (QT == kF32) {
         float* out = static_cast<float*>(a.out) + row * D + E * t;
 #pragma unroll
