@@ -1516,12 +1516,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
 
 // ---- tiled prefill for 16- and 8-bit pools: two blocks per step on 32x32 matrix steps ----
 //
-// The same work items, columns and order as paged_prefill_kernel (one wave
-// per (sequence, KV head, 32 / G new tokens), 32 query columns), with the
-// scores of 32 context tokens (two blocks) per step held as one 32x32 tile
-// S^T = K Q^T (tokens on rows, columns on columns) and the values taken with
-// 32x32x16 steps, O^T += V^T P^T, so both products run at the matrix cores'
-// full bf16 rate.
+// The columns of paged_prefill_kernel (a wave owns 32 / G new tokens of one
+// (sequence, KV head), 32 query columns), with the scores of 32 context
+// tokens (two blocks) per step held as one 32x32 tile S^T = K Q^T (tokens
+// on rows, columns on columns) and the values taken with 32x32x16 steps,
+// O^T += V^T P^T, so both products run at the matrix cores' full bf16 rate.
 //
 // Token order.  Row i of a step's score tile is block i / 16, token
 // swap_quads(i % 16), where swap_quads exchanges tokens 4-7 and 8-11 of a
@@ -1544,12 +1543,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kPrefillWave
 // less often; the normaliser is taken against the same reference, so the
 // result is unchanged.
 constexpr float kLazyMax = 8.0f;
-#ifndef PKV_PREFILL_CT
-#define PKV_PREFILL_CT 1
-#endif
-#ifndef PKV_PREFILL_LDS
-#define PKV_PREFILL_LDS 1
-#endif
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int swap_quads(int u) { return u ^ ((((u >> 2) ^ (u >> 3)) & 1) * 12); }
@@ -1568,15 +1561,6 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int KV, int D>
-struct Step32 {                      // K and V operands of one step (two blocks), per lane
-    static constexpr int NK = D / 16;  // QK steps (16 dimensions each)
-    static constexpr int NT = D / 32;  // output row tiles (32 dimensions each)
-    using KOp = typename std::conditional<KV == kBF16, uint4, uint2>::type;
-    KOp k[NK];
-    KOp v[NT][2];                    // [row tile][block]
-};
-
 template <int KV>
 __device__ __forceinline__ bf16x8 widen8(const typename std::conditional<KV == kBF16, uint4, uint2>::type& x) {
     if constexpr (KV == kBF16) {
@@ -1586,252 +1570,16 @@ __device__ __forceinline__ bf16x8 widen8(const typename std::conditional<KV == k
     }
 }
 
-template <int KV, int D, int CT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 2 : 1))) void paged_prefill32_kernel(
-    DecodeArgs a) {
-    using ST = Step32<KV, D>;
-    using KOp = typename ST::KOp;
-    constexpr int ELT = KV == kBF16 ? 2 : 1;
-    constexpr int TILE = kBlockTokens * D * ELT;
-    constexpr int NK = ST::NK, NT = ST::NT;
-    const int lane = lane_id(), n = lane & 31, h = lane >> 5;
-    const int G = a.group;
-    const int tpw = 32 * CT / G;  // new tokens per wave (columns past tpw * G hold none)
-    // work item: as paged_prefill_kernel
-    const uint32_t ntt = uint32_t((a.max_q + tpw - 1) / tpw);
-    const uint32_t kq = blockIdx.x / 8;
-    const uint32_t pair = blockIdx.x % 8 + 8 * (kq / ntt);
-    const int tt = int(ntt - 1 - kq % ntt);
-    if (pair >= uint32_t(a.num_seqs) * uint32_t(a.num_kv_heads)) return;
-    const int kvh = int(pair % uint32_t(a.num_kv_heads));
-    const int s = int(pair / uint32_t(a.num_kv_heads));
-    const int L = clamped_len(a, s);
-    const int q0 = a.cu_q[s];
-    const int nq = min(max(a.cu_q[s + 1] - q0, 0), L);
-    const int t0 = tt * tpw;
-    if (t0 >= nq) return;
-    const int tend = min(min(t0 + tpw, nq), a.max_q);  // tokens at index >= max_q are not computed
-    const int ctx = L - nq + tend;           // positions the wave's last token sees
-    const int vis_min = L - nq + t0 + 1;     // ... and its first token
-    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
-
-    // column tile c, column n: k = 32 c + n -> token t0 + k / G, head kvh * G + k % G (both lane halves hold
-    // the same column)
-    bool hv[CT];
-    int64_t row[CT];
-    int vis[CT];
-    bf16x8 qop[CT][NK];  // Q^T operands: column n, dimensions 16 i + 8 h .. + 7
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const int k = 32 * c + n;
-        const int tok = t0 + k / G;
-        hv[c] = k < tpw * G && tok < tend && q0 >= 0 && int64_t(q0) + tok < int64_t(a.num_q_rows);
-        row[c] = (hv[c] ? int64_t(q0) + tok : 0) * a.num_heads + kvh * G + k % G;
-        vis[c] = hv[c] ? L - nq + tok + 1 : ctx;
-        const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row[c] * D * 2;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const uint4 x = hv[c] ? *reinterpret_cast<const uint4*>(qrow + (16 * i + 8 * h) * 2) : make_uint4(0, 0, 0, 0);
-            qop[c][i] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-    f32x16 acc[CT][NT];
-    float mref[CT];  // reference maximum of each column (base-2 units)
-    float lsum[CT];  // this lane's share of each column's normaliser
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[c][t] = f32x16{};
-        mref[c] = kNegInf;
-        lsum[c] = 0.0f;
-    }
-
-    // Block ids are wave-uniform: read with scalar loads one step ahead of the K loads that use them (so
-    // the vector-load counter stays a plain count of tile loads and each wait covers exactly one set).
-    const int32_t* bt = a.block_table + int64_t(s) * a.max_blocks;
-    auto table_entry = [&](int j) -> int { return j < nblk ? bt[j] : -1; };
-    auto block_id = [&](int j, int id, int& nv) -> int {  // a table entry -> its block (0 if absent) and valid tokens
-        const bool ok = id >= 0 && id < a.num_blocks;
-        nv = ok ? min(kBlockTokens, L - j * kBlockTokens) : 0;
-        return ok ? id : 0;
-    };
-    const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + int64_t(kvh) * TILE;
-    const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + int64_t(kvh) * TILE;
-    const int64_t bstride = int64_t(a.num_kv_heads) * TILE;
-    // K operand of QK step i: token row n -> block n / 16, token swap_quads(n % 16), dimensions 16 i + 8 h ..
-    const int ktok = swap_quads(n & 15);
-    auto load_k = [&](ST& st, int id0, int id1) {
-        const uint8_t* kt = kbase + int64_t(n < 16 ? id0 : id1) * bstride;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if constexpr (KV == kBF16)
-                st.k[i] = *reinterpret_cast<const uint4*>(kt + ((2 * i + h) * kBlockTokens + ktok) * 16);
-            else
-                st.k[i] = *reinterpret_cast<const uint2*>(kt + (i * kBlockTokens + ktok) * 16 + 8 * h);
-        }
-    };
-    // V operand of row tile t, block b: dimension 32 t + n, tokens 8 h .. 8 h + 7
-    auto load_v = [&](ST& st, int id0, int id1) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint8_t* vt = vbase + int64_t(b == 0 ? id0 : id1) * bstride;
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                st.v[t][b] = *reinterpret_cast<const KOp*>(vt + ((32 * t + n) * kBlockTokens + 8 * h) * ELT);
-        }
-    };
-    const int nstep = (nblk + 1) / 2;
-    ST cur;     // K operands of the current step (the next step's load into them once consumed), V of even steps
-    ST other;   // V operands of odd steps (its K part is unused)
-    int nv0 = 0, nv1 = 0;
-    {
-        const int i0 = block_id(0, table_entry(0), nv0), i1 = block_id(1, table_entry(1), nv1);
-        load_k(cur, i0, i1);
-        load_v(cur, i0, i1);
-    }
-    const float cs = a.score_scale;
-    const float inv_cs = 1.0f / cs;
-    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float thr[CT];  // raw score above which a column's reference must move: (mref + kLazyMax) / scale
-#pragma unroll
-    for (int c = 0; c < CT; ++c) thr[c] = kNegInf;
-    // One step: the scores of two blocks, the next step's K and V loads (V into the other buffer, so a step's
-    // V has a whole step to arrive), the softmax update and the value products.
-    auto step = [&](int st, ST& vc, ST& vn) {
-        const int k0 = 32 * st;
-        const int e0 = table_entry(2 * st + 2), e1 = table_entry(2 * st + 3);  // the next step's blocks
-        // scores S^T = K Q^T, every column tile on each K operand
-        f32x16 sacc[CT];
-#pragma unroll
-        for (int c = 0; c < CT; ++c) sacc[c] = f32x16{};
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const bf16x8 kop = widen8<KV>(cur.k[i]);
-#pragma unroll
-            for (int c = 0; c < CT; ++c) sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c][i], sacc[c], 0, 0, 0);
-        }
-        // the next step's K loads, into the registers this step's K has left (after the last step they
-        // read block 0 and are never used: unconditional loads keep every wait a fixed count)
-        int nn0 = 0, nn1 = 0;
-        const int j0 = block_id(2 * st + 2, e0, nn0);
-        const int j1 = block_id(2 * st + 3, e1, nn1);
-        load_k(cur, j0, j1);
-        load_v(vn, j0, j1);
-        // masks: only where a block is short or absent, or the step reaches past a column's last position
-        const bool whole = nv0 == kBlockTokens && nv1 == kBlockTokens && k0 + 32 <= vis_min;
-        if (!whole) {
-#pragma unroll
-            for (int c = 0; c < CT; ++c)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tk = 8 * h + (i & 7);
-                    const int pos = k0 + 16 * (i >> 3) + tk;
-                    const bool ok = tk < (i < 8 ? nv0 : nv1) && pos < vis[c];
-                    sacc[c][i] = ok ? sacc[c][i] : kNegInf;
-                }
-            // values of absent tokens are zeroed (the pools may hold anything there)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int cnt = min(max((b == 0 ? nv0 : nv1) - 8 * h, 0), 8);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if constexpr (KV == kBF16) {
-                        uint4& x = vc.v[t][b];
-                        x.x = cnt >= 2 ? x.x : (cnt == 1 ? x.x & 0xffffu : 0u);
-                        x.y = cnt >= 4 ? x.y : (cnt == 3 ? x.y & 0xffffu : 0u);
-                        x.z = cnt >= 6 ? x.z : (cnt == 5 ? x.z & 0xffffu : 0u);
-                        x.w = cnt >= 8 ? x.w : (cnt == 7 ? x.w & 0xffffu : 0u);
-                    } else {
-                        uint2& x = vc.v[t][b];
-                        const uint32_t mlo = cnt >= 4 ? 0xffffffffu : (0xffffffffu >> (32 - 8 * cnt)) * (cnt > 0);
-                        const uint32_t mhi = cnt >= 8 ? 0xffffffffu : cnt > 4 ? (0xffffffffu >> (32 - 8 * (cnt - 4))) : 0u;
-                        x.x &= mlo;
-                        x.y &= mhi;
-                    }
-                }
-            }
-        }
-        bf16x8 pb[CT][2];  // exponentiated scores of block 0 and block 1, in the value steps' operand layout
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            // Does any score pass its column's threshold?  Only then is the column maximum (both halves)
-            // formed and the reference moved to it; the weights below are taken against the reference.
-            bool over = false;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) over = over || sacc[c][i] > thr[c];
-            if (__ballot(over)) {
-                float bm = fmaxf(fmaxf(fmaxf(sacc[c][0], sacc[c][1]), fmaxf(sacc[c][2], sacc[c][3])),
-                                 fmaxf(fmaxf(sacc[c][4], sacc[c][5]), fmaxf(sacc[c][6], sacc[c][7])));
-                bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sacc[c][8], sacc[c][9]), fmaxf(sacc[c][10], sacc[c][11])),
-                                     fmaxf(fmaxf(sacc[c][12], sacc[c][13]), fmaxf(sacc[c][14], sacc[c][15]))));
-                bm = halves_max(bm);
-                const float mnew = bm * cs;  // scale > 0: the maximum of the scaled scores (-inf stays -inf)
-                const bool move = mnew > mref[c] + kLazyMax;
-                const float mto = move ? mnew : mref[c];
-                const float alpha = !move ? 1.0f : mref[c] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mref[c] - mto);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[c][t] *= alpha;
-                lsum[c] *= alpha;
-                mref[c] = mto;
-                thr[c] = mto == kNegInf ? kNegInf : (mto + kLazyMax) * inv_cs;
-            }
-            const float mm = mref[c] == kNegInf ? 0.0f : mref[c];
-            uint32_t pk[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pk[e] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[c][2 * e], cs, -mm)),
-                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[c][2 * e + 1], cs, -mm)));
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                lsum[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), one2, lsum[c], false);
-            pb[c][0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            pb[c][1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-        }
-        // values O^T += V^T P^T, block 0 then block 1, every column tile on each V operand
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8 vop = widen8<KV>(vc.v[t][b]);
-#pragma unroll
-                for (int c = 0; c < CT; ++c) acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[c][b], acc[c][t], 0, 0, 0);
-            }
-        nv0 = nn0;
-        nv1 = nn1;
-    };
-    // Two steps per iteration, alternating the V buffers.  When the step count is odd the last one runs
-    // past the context: its blocks are absent, every score is masked and it adds nothing (kept
-    // unconditional so that every wait is a fixed count of loads).
-    for (int st = 0; st < nstep; st += 2) {
-        step(st, cur, other);
-        step(st + 1, other, cur);
-    }
-    // output: column n, dimensions 32 t + 8 b + 4 h + r
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-        const float lt = halves_sum(lsum[c]);
-        if (!hv[c]) continue;
-        const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-        uint16_t* o = static_cast<uint16_t*>(a.out) + row[c] * D;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                *reinterpret_cast<uint2*>(o + 32 * t + 8 * b + 4 * h) =
-                    make_uint2(pack_bf16(acc[c][t][4 * b] * inv, acc[c][t][4 * b + 1] * inv),
-                               pack_bf16(acc[c][t][4 * b + 2] * inv, acc[c][t][4 * b + 3] * inv));
-    }
-}
-
 // ---- the same prefill with K/V staged in LDS and shared by a workgroup of four waves ----
 //
 // A workgroup serves four consecutive token tiles (4 * 32 / G new tokens) of one (sequence, KV head); the
-// waves walk the same context, so each step's two K and two V tiles are brought in once for all four: wave w
-// copies one of the four tiles straight into LDS (gfx950 load-to-LDS, 16 bytes per lane, no registers),
-// and each wave reads its matrix operands from LDS.  Two LDS buffers alternate: step t + 1's tiles are in
-// flight while step t is computed, and one barrier per step separates the two uses of a buffer.  V tiles
-// are copied permuted, so that lane (n, h)'s operand (dimension row n of a 32-row tile, tokens 8h .. 8h + 7)
-// sits at 16 * lane within its 1 KiB (conflict-free reads); fp8 V tiles are copied as they are.
+// waves walk the same context, so each stage's K and V tiles (kPfSub 32-token steps, two blocks each) are
+// brought in once for all four: each wave copies a quarter of them straight into LDS (gfx950 load-to-LDS,
+// 16 bytes per lane, no registers), and each wave reads its matrix operands from LDS.  Two LDS buffers
+// alternate: stage s + 1's tiles are in flight while stage s is computed, and one barrier per stage
+// separates the two uses of a buffer.  V tiles are copied permuted, so that lane (n, h)'s operand
+// (dimension row n of a 32-row tile, tokens 8h .. 8h + 7) sits at 16 * lane within its 1 KiB
+// (conflict-free reads); fp8 V tiles are copied as they are.
 #ifndef PKV_PF_WAVES
 #define PKV_PF_WAVES 4
 #endif
@@ -2014,7 +1762,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(P
                 }
             }
         }
-        // lazy reference (see paged_prefill32_kernel)
+        // lazy reference (see the notes on the 32x32 steps above)
         bool over = false;
 #pragma unroll
         for (int i = 0; i < 16; ++i) over = over || sacc[i] > thr;
@@ -2079,16 +1827,9 @@ hipError_t launch_prefill_t(const DecodeArgs& a, int items, hipStream_t stream) 
         const int grid = (pairs + 7) / 8 * 8 * (items / pairs);
         hipLaunchKernelGGL((paged_prefill_kernel<KV, D, P>), dim3(grid), dim3(64), 0, stream, a);
     } else {
-#if PKV_PREFILL_LDS
         const int tpg = kPfWaves * (32 / a.group);
         const int grid = (pairs + 7) / 8 * 8 * ((a.max_q + tpg - 1) / tpg);
         hipLaunchKernelGGL((paged_prefill_lds_kernel<KV, D>), dim3(grid), dim3(64 * kPfWaves), 0, stream, a);
-#else
-        constexpr int CT = PKV_PREFILL_CT;
-        const int tpw = 32 * CT / a.group;
-        const int grid = (pairs + 7) / 8 * 8 * ((a.max_q + tpw - 1) / tpw);
-        hipLaunchKernelGGL((paged_prefill32_kernel<KV, D, CT>), dim3(grid), dim3(64), 0, stream, a);
-#endif
     }
     return hipGetLastError();
 }
