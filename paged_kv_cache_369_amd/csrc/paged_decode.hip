@@ -174,9 +174,10 @@ __device__ __forceinline__ void state_merge(State<NVC>& s, const State<NVC>& t) 
     const float ws = s.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s.m - M);
     const float wt = t.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(t.m - M);
     s.m = M;
-    s.l = s.l * ws + t.l * wt;
+    // explicit fused products, so that the same states merge to the same bits wherever this is inlined
+    s.l = __builtin_fmaf(t.l, wt, s.l * ws);
 #pragma unroll
-    for (int c = 0; c < NVC; ++c) s.acc[c] = s.acc[c] * ws + t.acc[c] * wt;
+    for (int c = 0; c < NVC; ++c) s.acc[c] = __builtin_elementwise_fma(t.acc[c], f32x4(wt), s.acc[c] * ws);
 }
 
 // Slot traffic between waves uses agent-coherent accesses (SC1: stores write
@@ -187,7 +188,43 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAgentCoherent = 16;  // SC1 cache-policy bit
 constexpr unsigned kRawBufferWord3 = 0x00020000u;
 
-template <int D, int NVC>
+// A slot holds m[16], l[16], then D values per head: acc in f32 for f32
+// queries; acc / l in bf16 for bf16 queries (a partial result rounded as an
+// output would be, half the bytes written through and read back), which the
+// load scales by l again.  In bf16 a lane moves chunks c and c + 1 in one
+// 16-byte access, and the four lanes of a column fill one 64-byte line per
+// access (lane (col, g) at col * D + 16 c + 8 g), so that the stores, which
+// write through, are whole lines.
+// Two chunks of a state's acc as stored in a bf16 slot (acc * inv, rounded to
+// nearest even), and back (times l).
+__device__ __forceinline__ u32x4 slot_pack(const f32x4& a, const f32x4& b, float inv) {
+    const f32x4 o0 = a * inv, o1 = b * inv;
+    return u32x4{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3]), pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+}
+
+__device__ __forceinline__ void slot_unpack(const u32x4& v, float l, f32x4& a, f32x4& b) {
+    const f32x4 o0 = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+                      __uint_as_float(v[1] & 0xffff0000u)};
+    const f32x4 o1 = {__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xffff0000u), __uint_as_float(v[3] << 16),
+                      __uint_as_float(v[3] & 0xffff0000u)};
+    a = o0 * l;
+    b = o1 * l;
+}
+
+__device__ __forceinline__ float slot_inv(float l) { return l > 0.0f ? 1.0f / l : 0.0f; }
+
+// A state as it would come back from a slot: a merge then gives the same bits
+// whichever member's state stayed in the wave.
+template <int QT, int NVC>
+__device__ __forceinline__ void state_round(State<NVC>& s) {
+    if constexpr (QT != kF32) {
+        const float inv = slot_inv(s.l);
+#pragma unroll
+        for (int c = 0; c < NVC; c += 2) slot_unpack(slot_pack(s.acc[c], s.acc[c + 1], inv), s.l, s.acc[c], s.acc[c + 1]);
+    }
+}
+
+template <int QT, int D, int NVC>
 __device__ __forceinline__ void state_store(float* f, int slot_bytes, const State<NVC>& s, bool hv) {
     const int lane = lane_id(), g = lane >> 4, col = lane & 15;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(f, 0, slot_bytes, kRawBufferWord3);
@@ -196,13 +233,23 @@ __device__ __forceinline__ void state_store(float* f, int slot_bytes, const Stat
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.m), r, col * 4, 0, kAgentCoherent);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.l), r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent);
     }
-    const int ab = (kSlotHead + col * D + 4 * g) * 4;
+    if constexpr (QT == kF32) {
+        const int ab = (kSlotHead + col * D + 4 * g) * 4;
 #pragma unroll
-    for (int c = 0; c < NVC; ++c)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r, ab + 64 * c, 0, kAgentCoherent);
+        for (int c = 0; c < NVC; ++c)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r, ab + 64 * c, 0,
+                                                   kAgentCoherent);
+    } else {
+        const int ab = kSlotHead * 4 + (col * D + 8 * g) * 2;
+        const float inv = slot_inv(s.l);
+#pragma unroll
+        for (int c = 0; c < NVC; c += 2)
+            __builtin_amdgcn_raw_buffer_store_b128(slot_pack(s.acc[c], s.acc[c + 1], inv), r, ab + 32 * c, 0,
+                                                   kAgentCoherent);
+    }
 }
 
-template <int D, int NVC>
+template <int QT, int D, int NVC>
 __device__ __forceinline__ void state_load(const float* f, int slot_bytes, State<NVC>& s, bool hv) {
     const int lane = lane_id(), g = lane >> 4;
     const int col = hv ? (lane & 15) : 0;  // lanes without a head read head 0's data and never store it
@@ -210,43 +257,58 @@ __device__ __forceinline__ void state_load(const float* f, int slot_bytes, State
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(f), 0, slot_bytes, kRawBufferWord3);
     s.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, col * 4, 0, kAgentCoherent));
     s.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent));
-    const int ab = (kSlotHead + col * D + 4 * g) * 4;
+    if constexpr (QT == kF32) {
+        const int ab = (kSlotHead + col * D + 4 * g) * 4;
 #pragma unroll
-    for (int c = 0; c < NVC; ++c)
-        s.acc[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * c, 0, kAgentCoherent));
-}
-
-// State rows of the shared-prefix meeting: one row per (sequence, head) with
-// acc[D] first, then m and l.  Each lane moves its column's row; the same
-// agent-coherent accesses as the slots.
-template <int D, int NVC>
-__device__ __forceinline__ void row_store(float* base, int bytes, int64_t row, const State<NVC>& s, bool on) {
-    const int g = lane_id() >> 4;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRawBufferWord3);
-    if (!on) return;
-    const int off = int(row) * (D + 4) * 4;
+        for (int c = 0; c < NVC; ++c)
+            s.acc[c] =
+                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * c, 0, kAgentCoherent));
+    } else {
+        const int ab = kSlotHead * 4 + (col * D + 8 * g) * 2;
 #pragma unroll
-    for (int c = 0; c < NVC; ++c)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r, off + (16 * c + 4 * g) * 4, 0,
-                                               kAgentCoherent);
-    if (g == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.m), r, off + D * 4, 0, kAgentCoherent);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.l), r, off + (D + 1) * 4, 0, kAgentCoherent);
+        for (int c = 0; c < NVC; c += 2)
+            slot_unpack(__builtin_amdgcn_raw_buffer_load_b128(r, ab + 32 * c, 0, kAgentCoherent), s.l, s.acc[c],
+                        s.acc[c + 1]);
     }
 }
 
-template <int D, int NVC>
-__device__ __forceinline__ void row_load(const float* base, int bytes, int64_t row, State<NVC>& s, bool on) {
+// The dimension held at position p of a bf16 slot column or state row: 16-byte
+// group p / 8 holds chunk 2 (p / 32) + (p / 4) % 2 of lane g = (p / 8) % 4.
+__device__ __forceinline__ int row_dim(int p) { return 16 * (2 * (p / 32) + (p / 4) % 2) + 4 * ((p / 8) % 4) + p % 4; }
+
+// State rows of the shared-prefix decode: for `rows` = num_seqs * num_heads
+// (row = sequence * num_heads + head), the output-shaped part of every row
+// first, then the (m, l) pairs of every row, so that each row's first part is
+// whole 64-byte lines.  With f32 queries the first part is acc[D] in f32; with
+// bf16 queries it is acc / l in bf16 (the partial result rounded as an output
+// would be, half the bytes to write and read again), in a slot column's order.
+// Each lane moves its column's row; the same agent-coherent accesses as the
+// slots.
+template <int QT, int D, int NVC>
+__device__ __forceinline__ void row_store(float* base, int bytes, int64_t rows, int64_t row, const State<NVC>& s,
+                                          bool on) {
+    constexpr int EB = QT == kF32 ? 4 : 2;  // bytes per element of the first part
     const int g = lane_id() >> 4;
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, kRawBufferWord3);
-    const int off = on ? int(row) * (D + 4) * 4 : 0;  // lanes without a row read row 0 and never use it
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRawBufferWord3);
+    if (!on) return;
+    const int off = int(row) * D * EB;
+    if constexpr (QT == kF32) {
 #pragma unroll
-    for (int c = 0; c < NVC; ++c)
-        s.acc[c] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + (16 * c + 4 * g) * 4, 0, kAgentCoherent));
-    s.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + D * 4, 0, kAgentCoherent));
-    s.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + (D + 1) * 4, 0, kAgentCoherent));
+        for (int c = 0; c < NVC; ++c)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s.acc[c]), r,
+                                                   off + (16 * c + 4 * g) * 4, 0, kAgentCoherent);
+    } else {  // the order of a bf16 slot column (row_dim gives a position's dimension)
+        const float inv = slot_inv(s.l);
+#pragma unroll
+        for (int c = 0; c < NVC; c += 2)
+            __builtin_amdgcn_raw_buffer_store_b128(slot_pack(s.acc[c], s.acc[c + 1], inv), r, off + (16 * c + 8 * g) * 2,
+                                                   0, kAgentCoherent);
+    }
+    if (g == 0) {
+        const int mo = int(rows * D * EB + 8 * row);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.m), r, mo, 0, kAgentCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s.l), r, mo + 4, 0, kAgentCoherent);
+    }
 }
 
 // A wave's merged state of the partitions it has finished of the current run
@@ -852,7 +914,7 @@ __device__ __forceinline__ int peek_arrivals(const DecodeArgs& a, const Contrib&
 
 // Returns true in the one wave that ends up with the run's whole state (left
 // in own_state).
-template <int D, int NVC>
+template <int QT, int D, int NVC>
 __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, const State<NVC>& mine,
                              LdsState<NVC>& own_state, bool hv, int seen) {
     auto slot = [&](uint32_t i) { return slot_ptr(a, c.w0 + i, (i == 0 && c.first_in_slot1) ? 1 : 0); };
@@ -872,7 +934,7 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
                 {
                     State<NVC> t;
                     lds_get(own_state, t);
-                    state_store<D>(slot(idx * span), slot_bytes, t, hv);
+                    state_store<QT, D>(slot(idx * span), slot_bytes, t, hv);
                 }
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 __builtin_amdgcn_s_waitcnt(0);  // the state has reached the coherent level before it is counted
@@ -893,10 +955,11 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
                 if (k == own) {
                     State<NVC> o;
                     lds_get(own_state, o);
+                    state_round<QT>(o);
                     state_merge(res, o);
                 } else {
                     State<NVC> in;
-                    state_load<D>(slot((first + k) * span), slot_bytes, in, hv);
+                    state_load<QT, D>(slot((first + k) * span), slot_bytes, in, hv);
                     state_merge(res, in);
                 }
             }
@@ -917,12 +980,13 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
 // written straight from the prefix run; uncovered sequences are plain runs.
 template <int QT, int D, int NVC>
 __device__ void finish_suffix(const DecodeArgs& a, const Cols& cm, const State<NVC>& st) {
-    row_store<D>(a.sstate, a.state_bytes, cm.row, st, cm.hv);
+    row_store<QT, D>(a.sstate, a.state_bytes, int64_t(a.num_seqs) * a.num_heads, cm.row, st, cm.hv);
 }
 
 template <int QT, int D, int NVC>
 __device__ void finish_prefix(const DecodeArgs& a, const Cols& cm, const State<NVC>& st) {
-    row_store<D>(a.pstate, a.state_bytes, cm.row, st, cm.hv && cm.sne);  // rows whose sequence has suffix runs
+    // rows whose sequence has suffix runs
+    row_store<QT, D>(a.pstate, a.state_bytes, int64_t(a.num_seqs) * a.num_heads, cm.row, st, cm.hv && cm.sne);
     state_output<QT, D>(a, cm.row, st, cm.hv && !cm.sne);               // the rest: the prefix state is whole
 }
 
@@ -1290,7 +1354,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
                 holding = false;
                 bool whole = (f & kLocal) != 0;
                 if (!whole &&
-                    merge_across<D>(a, unpack_contrib(sl[0].contrib), sw, st, held, cm.hv, seen)) {
+                    merge_across<QT, D>(a, unpack_contrib(sl[0].contrib), sw, st, held, cm.hv, seen)) {
                     lds_get(held, st);
                     whole = true;
                 }
@@ -1853,24 +1917,39 @@ __global__ __launch_bounds__(32 * kMergeRows) void cascade_merge_kernel(DecodeAr
     const int s = int(row / a.num_heads);
     // the two rows are read before the sharing arrays are (both are in bounds for any row), so that
     // their loads overlap the dependent reads that decide whether the row is merged at all
-    using VE = typename std::conditional<E == 4, float4, float2>::type;
-    const float* pr = a.pstate + row * (D + 4);
-    const float* sr = a.sstate + row * (D + 4);
-    const VE pv = *reinterpret_cast<const VE*>(pr + E * t);
-    const VE sv = *reinterpret_cast<const VE*>(sr + E * t);
-    const float2 pml = *reinterpret_cast<const float2*>(pr + D);
-    const float2 sml = *reinterpret_cast<const float2*>(sr + D);
+    // a row's first part: E f32 of acc (f32 queries) or E bf16 of acc / l (bf16 queries) per thread
+    constexpr int EB = QT == kF32 ? 4 : 2;
+    using VE = typename std::conditional<E * EB == 16, uint4, typename std::conditional<E * EB == 8, uint2, uint32_t>::type>::type;
+    const int64_t rows = int64_t(a.num_seqs) * a.num_heads;
+    const char* pb = reinterpret_cast<const char*>(a.pstate);
+    const char* sb = reinterpret_cast<const char*>(a.sstate);
+    const VE pv = *reinterpret_cast<const VE*>(pb + (row * D + E * t) * EB);
+    const VE sv = *reinterpret_cast<const VE*>(sb + (row * D + E * t) * EB);
+    const float2 pml = *reinterpret_cast<const float2*>(pb + rows * D * EB + 8 * row);
+    const float2 sml = *reinterpret_cast<const float2*>(sb + rows * D * EB + 8 * row);
     const SeqInfo si = seq_info<kModeShared>(a, s);
     const int nb = (si.len + kBlockTokens - 1) / kBlockTokens;
     if (si.cl < 0 || nb <= si.pbe) return;  // not covered, or no suffix runs: written by the decode
     const float mp = pml.x, lp = pml.y, ms = sml.x, ls = sml.y;
     float pa[E], sa[E];
-    __builtin_memcpy(pa, &pv, sizeof(pa));
-    __builtin_memcpy(sa, &sv, sizeof(sa));
+    if constexpr (QT == kF32) {
+        __builtin_memcpy(pa, &pv, sizeof(pa));
+        __builtin_memcpy(sa, &sv, sizeof(sa));
+    } else {
+        uint16_t ph[E], sh[E];
+        __builtin_memcpy(ph, &pv, sizeof(ph));
+        __builtin_memcpy(sh, &sv, sizeof(sh));
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            pa[e] = __uint_as_float(uint32_t(ph[e]) << 16);
+            sa[e] = __uint_as_float(uint32_t(sh[e]) << 16);
+        }
+    }
     const float M = fmaxf(mp, ms);
-    const float wp = mp == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
-    const float ws = ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-    const float l = lp * wp + ls * ws;
+    // the weight of each part: exp(m - M) times what its first part was divided by (1 for acc)
+    const float wp = mp == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mp - M) * (QT == kF32 ? 1.0f : lp);
+    const float ws = ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ms - M) * (QT == kF32 ? 1.0f : ls);
+    const float l = QT == kF32 ? lp * wp + ls * ws : wp + ws;
     const float inv = l > 0.0f ? a.v_scale / l : 0.0f;
     float o[E];
 #pragma unroll
@@ -1879,8 +1958,8 @@ __global__ __launch_bounds__(32 * kMergeRows) void cascade_merge_kernel(DecodeAr
         float* out = static_cast<float*>(a.out) + row * D + E * t;
 #pragma unroll
         for (int e = 0; e < E; ++e) out[e] = o[e];
-    } else {
-        uint16_t* out = static_cast<uint16_t*>(a.out) + row * D + E * t;
+    } else {  // positions E t .. E t + E - 1 of a bf16 row are E consecutive dimensions
+        uint16_t* out = static_cast<uint16_t*>(a.out) + row * D + row_dim(E * t);
 #pragma unroll
         for (int e = 0; e < E; e += 2) *reinterpret_cast<uint32_t*>(out + e) = pack_bf16(o[e], o[e + 1]);
     }

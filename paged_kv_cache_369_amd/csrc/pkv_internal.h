@@ -116,9 +116,11 @@ struct DecodeArgs {
 // with shared prefixes read once, or several new query tokens per sequence.
 enum Mode : int { kModePlain = 0, kModeShared = 1, kModeMulti = 2 };
 
-// Shared-prefix state rows, after the slots: two arrays (prefix, suffix) of
-// num_seqs * num_heads rows (row = sequence * num_heads + head) of head_dim + 4
-// floats: acc[head_dim], m, l, two unused.
+// Shared-prefix state rows, after the slots: two arrays (prefix, suffix), each
+// sized num_seqs * num_heads rows of head_dim + 4 floats.  Each holds the first
+// part of every row (row = sequence * num_heads + head) -- acc[head_dim] in f32
+// for f32 queries, acc / l in bf16 for bf16 queries -- then the (m, l) float
+// pair of every row; the rest is unused.
 inline int64_t align_floats(int64_t n) { return (n + 63) / 64 * 64; }
 inline int64_t state_row_floats(int head_dim) { return int64_t(head_dim) + 4; }
 
