@@ -213,17 +213,6 @@ __device__ __forceinline__ void slot_unpack(const u32x4& v, float l, f32x4& a, f
 
 __device__ __forceinline__ float slot_inv(float l) { return l > 0.0f ? 1.0f / l : 0.0f; }
 
-// A state as it would come back from a slot: a merge then gives the same bits
-// whichever member's state stayed in the wave.
-template <int QT, int NVC>
-__device__ __forceinline__ void state_round(State<NVC>& s) {
-    if constexpr (QT != kF32) {
-        const float inv = slot_inv(s.l);
-#pragma unroll
-        for (int c = 0; c < NVC; c += 2) slot_unpack(slot_pack(s.acc[c], s.acc[c + 1], inv), s.l, s.acc[c], s.acc[c + 1]);
-    }
-}
-
 template <int QT, int D, int NVC>
 __device__ __forceinline__ void state_store(float* f, int slot_bytes, const State<NVC>& s, bool hv) {
     const int lane = lane_id(), g = lane >> 4, col = lane & 15;
@@ -249,26 +238,49 @@ __device__ __forceinline__ void state_store(float* f, int slot_bytes, const Stat
     }
 }
 
+// A member's slot as loaded, before it is widened into a State: its m, l and
+// its values (f32 acc, or bf16 acc / l two chunks per access), so that the
+// loads of the next members can be in flight while one is merged.
+template <int QT, int NVC>
+struct SlotRead {
+    static constexpr int NQ = QT == kF32 ? NVC : NVC / 2;  // 16-byte accesses per lane
+    float m, l;
+    u32x4 v[NQ];
+};
+
 template <int QT, int D, int NVC>
-__device__ __forceinline__ void state_load(const float* f, int slot_bytes, State<NVC>& s, bool hv) {
+__device__ __forceinline__ void slot_fetch(const float* f, int slot_bytes, bool hv, SlotRead<QT, NVC>& x) {
     const int lane = lane_id(), g = lane >> 4;
     const int col = hv ? (lane & 15) : 0;  // lanes without a head read head 0's data and never store it
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(f), 0, slot_bytes, kRawBufferWord3);
-    s.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, col * 4, 0, kAgentCoherent));
-    s.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent));
-    if constexpr (QT == kF32) {
-        const int ab = (kSlotHead + col * D + 4 * g) * 4;
+    x.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, col * 4, 0, kAgentCoherent));
+    x.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (kMaxRunHeads + col) * 4, 0, kAgentCoherent));
+    const int ab = QT == kF32 ? (kSlotHead + col * D + 4 * g) * 4 : kSlotHead * 4 + (col * D + 8 * g) * 2;
 #pragma unroll
-        for (int c = 0; c < NVC; ++c)
-            s.acc[c] =
-                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * c, 0, kAgentCoherent));
-    } else {
-        const int ab = kSlotHead * 4 + (col * D + 8 * g) * 2;
+    for (int q = 0; q < SlotRead<QT, NVC>::NQ; ++q)
+        x.v[q] = __builtin_amdgcn_raw_buffer_load_b128(r, ab + 64 * q, 0, kAgentCoherent);
+}
+
+// res <- merge(res, x), x widened one access at a time (the same operations as
+// state_merge on the state a slot load gives).
+template <int QT, int NVC>
+__device__ __forceinline__ void merge_slot(State<NVC>& res, const SlotRead<QT, NVC>& x) {
+    const float M = fmaxf(res.m, x.m);
+    const float ws = res.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(res.m - M);
+    const float wt = x.m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(x.m - M);
+    res.m = M;
+    res.l = __builtin_fmaf(x.l, wt, res.l * ws);
 #pragma unroll
-        for (int c = 0; c < NVC; c += 2)
-            slot_unpack(__builtin_amdgcn_raw_buffer_load_b128(r, ab + 32 * c, 0, kAgentCoherent), s.l, s.acc[c],
-                        s.acc[c + 1]);
+    for (int q = 0; q < SlotRead<QT, NVC>::NQ; ++q) {
+        if constexpr (QT == kF32) {
+            res.acc[q] = __builtin_elementwise_fma(__builtin_bit_cast(f32x4, x.v[q]), f32x4(wt), res.acc[q] * ws);
+        } else {
+            f32x4 a, b;
+            slot_unpack(x.v[q], x.l, a, b);
+            res.acc[2 * q] = __builtin_elementwise_fma(a, f32x4(wt), res.acc[2 * q] * ws);
+            res.acc[2 * q + 1] = __builtin_elementwise_fma(b, f32x4(wt), res.acc[2 * q + 1] * ws);
+        }
     }
 }
 
@@ -912,6 +924,25 @@ __device__ __forceinline__ int peek_arrivals(const DecodeArgs& a, const Contrib&
     return seen;
 }
 
+// The state a wave keeps in LDS, in the form its slot would hold (so that a
+// merge gives the same bits whichever member kept its state).
+template <int QT, int NVC>
+__device__ __forceinline__ void slot_own(const LdsState<NVC>& o, SlotRead<QT, NVC>& x) {
+    const int lane = lane_id();
+    x.m = o.m[lane];
+    x.l = o.l[lane];
+    auto chunk = [&](int c) {
+        return f32x4{o.acc[4 * c][lane], o.acc[4 * c + 1][lane], o.acc[4 * c + 2][lane], o.acc[4 * c + 3][lane]};
+    };
+#pragma unroll
+    for (int q = 0; q < SlotRead<QT, NVC>::NQ; ++q) {
+        if constexpr (QT == kF32)
+            x.v[q] = __builtin_bit_cast(u32x4, chunk(q));
+        else
+            x.v[q] = slot_pack(chunk(2 * q), chunk(2 * q + 1), slot_inv(x.l));
+    }
+}
+
 // Returns true in the one wave that ends up with the run's whole state (left
 // in own_state).
 template <int QT, int D, int NVC>
@@ -946,22 +977,29 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
             if (!last) return false;  // a later arrival completes the group
             if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below are issued after the count was seen
-            // members in index order, one state per round trip; this wave's own from LDS
+            // Members in index order, this wave's own from LDS; the slots of the
+            // next two members load while one merges.  Every pass issues its
+            // loads (past the group they read the last member's slot again,
+            // unused), so the loads never sit behind a branch.
             const uint32_t own = idx - first;
+            auto fetch = [&](SlotRead<QT, NVC>& x, uint32_t k) {
+                slot_fetch<QT, D>(slot((first + min(k, members - 1)) * span), slot_bytes, hv, x);
+            };
             State<NVC> res;
             state_clear(res);
+            SlotRead<QT, NVC> xa, xb;
+            fetch(xa, 0);
+            fetch(xb, 1);
 #pragma unroll 1
-            for (uint32_t k = 0; k < members; ++k) {
-                if (k == own) {
-                    State<NVC> o;
-                    lds_get(own_state, o);
-                    state_round<QT>(o);
-                    state_merge(res, o);
-                } else {
-                    State<NVC> in;
-                    state_load<QT, D>(slot((first + k) * span), slot_bytes, in, hv);
-                    state_merge(res, in);
+            for (uint32_t k = 0; k < members; k += 2) {
+                if (k == own) slot_own(own_state, xa);
+                merge_slot(res, xa);
+                fetch(xa, k + 2);
+                if (k + 1 < members) {
+                    if (k + 1 == own) slot_own(own_state, xb);
+                    merge_slot(res, xb);
                 }
+                fetch(xb, k + 3);
             }
             lds_put(own_state, res);
         }
