@@ -32,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import ctypes
 import glob
 import hashlib
 import json
@@ -551,6 +552,66 @@ def oracle_baseline(w, out_dev, q_dtype, max_seqs: int):
     return n, rows, dt, times, oracle.num_threads(0), err
 
 
+def timeline_summary(rows, kv_bytes: int, desc: str, command: str) -> str:
+    """Markdown summary of one decode call's per-wave stamps (pkv_timeline_read rows: entry, first tile,
+    1/4, 1/2, 3/4 of the tiles, end in 100 MHz ticks; hardware wave id | XCD << 32 | tiles << 40; last tile)."""
+    r = rows[rows[:, 0] != 0].astype(np.int64)
+    t0 = r[:, 0].min()
+    us = (r[:, :6] - t0) / 100.0  # microseconds after the first wave's entry
+    ent, first, q1, q2, q3, end = (us[:, i] for i in range(6))
+    hw = r[:, 6] & 0xffffffff
+    xcc = (r[:, 6] >> 32) & 0xf
+    tiles = r[:, 6] >> 40
+    last = (r[:, 7] - t0) / 100.0
+    slot = hw & 0xf
+    n = len(r)
+    out = [f"# Per-wave timeline of one decode call, {desc}", "",
+           "Command (run from the repository root; the instrumented library is the same sources with "
+           "PKV_TIMELINE defined, each wave adding six clock reads and one 64-byte store):", "",
+           f"    {command}", "",
+           f"{n} waves with a stretch; times in µs after the first wave's entry (real-time clock, 100 MHz). "
+           f"Last wave ends at {end.max():.1f} µs.", "",
+           "| wave slot | waves | entry p50 | first tile p50 | 25 % p50 | 50 % p50 | 75 % p50 | last tile p50 | "
+           "end p10 | end p50 | end p90 | end max | close after last tile p50 / p90 / max |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    med = lambda x: float(np.median(x)) if len(x) else float("nan")
+    pct = lambda x, p: float(np.percentile(x, p)) if len(x) else float("nan")
+    for sl in sorted(set(slot.tolist())):
+        m = slot == sl
+        cl = end[m] - last[m]
+        out.append(f"| {sl} | {int(m.sum())} | {med(ent[m]):.1f} | {med(first[m]):.1f} | {med(q1[m]):.1f} | "
+                   f"{med(q2[m]):.1f} | {med(q3[m]):.1f} | {med(last[m]):.1f} | {pct(end[m], 10):.1f} | "
+                   f"{med(end[m]):.1f} | {pct(end[m], 90):.1f} | {end[m].max():.1f} | "
+                   f"{med(cl):.1f} / {pct(cl, 90):.1f} / {cl.max():.1f} |")
+    out += ["", "Mean end by XCD and wave slot (µs):", "",
+            "| XCD | " + " | ".join(f"slot {sl}" for sl in sorted(set(slot.tolist()))) + " |",
+            "|---|" + "---|" * len(set(slot.tolist()))]
+    for x in sorted(set(xcc.tolist())):
+        cells = []
+        for sl in sorted(set(slot.tolist())):
+            m = (xcc == x) & (slot == sl)
+            cells.append(f"{end[m].mean():.1f}" if m.any() else "-")
+        out.append(f"| {x} | " + " | ".join(cells) + " |")
+    # aggregate rate: each wave's tiles done, linear between its stamps, times the mean bytes per tile
+    bpt = kv_bytes / max(int(tiles.sum()), 1)
+    marks = np.stack([first, q1, q2, q3, np.maximum(last, q3)], axis=1)
+    done = np.stack([np.minimum(1, tiles), np.maximum(1, tiles // 4), np.maximum(2, tiles // 2),
+                     np.maximum(3, tiles * 3 // 4), tiles], axis=1).astype(np.float64)
+    step = 10.0
+    edges = np.arange(0.0, end.max() + step, step)
+    prog = np.array([sum(np.interp(t, marks[i], done[i], left=0.0, right=float(tiles[i])) for i in range(n))
+                     for t in edges])
+    out += ["", f"Aggregate KV rate per {step:.0f} µs window (each wave's tiles interpolated between its stamps, "
+            f"{bpt / 1024:.2f} KiB per tile on average), waves still running, and those of them that have consumed "
+            f"their last tile (closing and merging their last state):", "",
+            "| window (µs) | TB/s | waves running | of them past their last tile |", "|---|---|---|---|"]
+    for a, b, pa, pb in zip(edges[:-1], edges[1:], prog[:-1], prog[1:]):
+        running = int(((ent <= b) & (end > a)).sum())
+        closing = int(((last <= a) & (end > a)).sum())
+        out.append(f"| {a:.0f}–{b:.0f} | {(pb - pa) * bpt / (step * 1e-6) / 1e12:.2f} | {running} | {closing} |")
+    return "\n".join(out) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,6 +636,10 @@ def main() -> int:
     ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
                     help="read (or overwrite) 512 MB before every step, outside the timed brackets, so the step's "
                          "KV reads cannot hit what the previous step left in the 256 MB infinity cache")
+    ap.add_argument("--timeline", action="store_true",
+                    help="run the instrumented library (python -m paged_kv_cache_369_amd.build --timeline) and "
+                         "write a per-wave timeline summary of one decode call to --timeline-out")
+    ap.add_argument("--timeline-out", default=None, help="where --timeline writes (default profiles/)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode step, run a plain device copy of known size (counter scale)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a markdown summary of a rocprofv3 --stats run")
@@ -612,6 +677,14 @@ def main() -> int:
     import torch
     import paged_kv_cache_369_amd as pkv
     from paged_kv_cache_369_amd import workloads as W
+
+    if args.timeline:
+        from paged_kv_cache_369_amd import build as pkv_build
+        if not os.path.exists(pkv_build.OUT_TIMELINE):
+            print(f"{pkv_build.OUT_TIMELINE} is not built: python -m paged_kv_cache_369_amd.build --timeline",
+                  file=sys.stderr)
+            return 2
+        pkv._LIB_PATH = pkv_build.OUT_TIMELINE
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -709,6 +782,33 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    if args.timeline:
+        # one more step after the timed ones, its decode waves' stamps read back
+        lib = pkv._load()
+        lib.pkv_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        if lib.pkv_timeline_clear() != 0:
+            raise RuntimeError("pkv_timeline_clear failed")
+        write()
+        decode()
+        torch.cuda.synchronize()
+        rows = np.zeros((4096, 8), dtype=np.uint64)
+        if lib.pkv_timeline_read(rows.ctypes.data, 4096) != 0:
+            raise RuntimeError("pkv_timeline_read failed")
+        kvb = (cascade_read_bytes(w) if args.cascade else varlen_read_bytes(w) if multi else w.kv_bytes())
+        argv, skip = [], False
+        for a in sys.argv[1:]:  # the command as run, without where it wrote
+            if skip or a.startswith("--timeline-out"):
+                skip = a == "--timeline-out"
+                continue
+            argv.append(a)
+        cmd = "python -m paged_kv_cache_369_amd.build --timeline && python3 bench.py " + " ".join(argv)
+        text = timeline_summary(rows, kvb, WORKLOAD_DESC[args.workload] + (CASCADE_NOTE if args.cascade else ""),
+                                cmd)
+        path = args.timeline_out or os.path.join(PROFILES, f"paged_decode_{profile_key(args)}_timeline.md")
+        with open(path, "w") as f:
+            f.write(text)
+        print(text)
+        return 0
     if flush is not None:  # the flush is not part of the step: time the step from its events
         ms_per_step = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
     t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3

@@ -64,6 +64,19 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Per-wave timeline, compiled only into the instrumented library (PKV_TIMELINE):
+// for each decode wave the real-time clock (100 MHz) at entry, after its first
+// tile, after 1/4, 1/2 and 3/4 of its tiles and at its end, then its hardware
+// wave id | XCD << 32 | tile count << 40, then the clock after its last tile
+// (before the state it closes is merged and written).  Lane 0 writes the eight
+// words once, at the end; waves without a stretch write nothing.
+#ifdef PKV_TIMELINE
+__device__ unsigned long long g_timeline[kMaxWaves * 8];
+#define PKV_TL(...) __VA_ARGS__
+#else
+#define PKV_TL(...)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -551,13 +564,6 @@ struct Cols {
     bool sne;     // prefix runs: that head's sequence also has suffix runs
 };
 
-// Columns of a plain or suffix run (s, hg): heads hg * rh + col, col < rh.
-__device__ __forceinline__ Cols plain_cols(const DecodeArgs& a, int s, int hg) {
-    const int col = lane_id() & 15;
-    const bool hv = col < a.rh;
-    return Cols{int64_t(s) * a.num_heads + hg * a.rh + (hv ? col : 0), hv, false};
-}
-
 // Columns of prefix run (s, hg): column col serves head hg * rh + col % rh of
 // sequence s + col / rh, if that sequence is covered by s's prefix runs.
 template <int M>
@@ -977,6 +983,7 @@ __device__ bool merge_across(const DecodeArgs& a, const Contrib& c, uint32_t w, 
             if (!last) return false;  // a later arrival completes the group
             if (lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below are issued after the count was seen
+
             // Members in index order, this wave's own from LDS; the slots of the
             // next two members load while one merges.  Every pass issues its
             // loads (past the group they read the last member's slot again,
@@ -1102,6 +1109,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     const uint32_t w = blockIdx.x;
     const uint32_t nwt = gridDim.x;
     const int lane = lane_id();
+    PKV_TL(const unsigned long long tl_entry = __builtin_amdgcn_s_memrealtime();)
 
     // ---- total units; per-chunk totals of the first kLenChunks chunks; rows
     //      of empty sequences are zeroed (sequence s by wave s mod grid) ----
@@ -1432,6 +1440,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
     int lrb[P];  // tokens of the context at and after the buffered block's first token
 #pragma unroll
     for (int k = 0; k < P - 1; ++k) issue(buf[k], nvb[k], lrb[k], uint32_t(k));
+    PKV_TL(unsigned long long tl[6] = {tl_entry, 0, 0, 0, 0, 0}; const uint32_t tl_n = hi - lo; int tl_k = 0;
+           uint32_t tl_next = 1; unsigned long long tl_last = 0;)
     bool more = true;
     for (uint32_t t = 0; more; t += P) {
 #pragma unroll
@@ -1441,10 +1451,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSim
             if (more) {
                 issue(buf[(k + P - 1) % P], nvb[(k + P - 1) % P], lrb[(k + P - 1) % P], tp + uint32_t(P - 1));
                 consume_tile<KV, D, M == kModeMulti>(a, buf[k], nvb[k], lrb[k] + crel, qop, rs);
+                PKV_TL(if (tp + 1 == tl_next && tl_k < 4) {
+                    tl[1 + tl_k] = __builtin_amdgcn_s_memrealtime();
+                    ++tl_k;
+                    tl_next = max(tl_next + 1, uint32_t(uint64_t(tl_n) * uint32_t(tl_k) / 4));
+                } if (tp + 1 == tl_n) tl_last = __builtin_amdgcn_s_memrealtime();)
                 if (tp + 1 == sl[0].p1) next_piece();
             }
         }
     }
+    PKV_TL({
+        tl[5] = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) {
+            const uint32_t hwid = __builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_ID
+            const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+            unsigned long long* o = g_timeline + uint64_t(w) * 8;
+            for (int e = 0; e < 6; ++e) o[e] = tl[e];
+            o[6] = uint64_t(hwid) | (uint64_t(xcc & 0xf) << 32) | (uint64_t(tl_n) << 40);
+            o[7] = tl_last;
+        }
+    })
 }
 
 // Pipeline depth per pool type: enough K/V tiles in flight per wave to cover
@@ -2102,3 +2128,23 @@ hipError_t noalloc_scratch(float** out, hipStream_t stream) {
 }
 
 }  // namespace pkv
+
+#ifdef PKV_TIMELINE
+// Instrumented library only: copy the first n_waves rows of eight words of the
+// last decode call's timeline to host memory (after the call has finished).
+extern "C" int pkv_timeline_read(unsigned long long* host, int n_waves) {
+    if (!host || n_waves < 0 || n_waves > pkv::kMaxWaves) return 1;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(pkv::g_timeline), size_t(n_waves) * 64, 0, hipMemcpyDeviceToHost) ==
+                   hipSuccess
+               ? 0
+               : 2;
+}
+
+extern "C" int pkv_timeline_clear() {
+    static unsigned long long zeros[pkv::kMaxWaves * 8];
+    return hipMemcpyToSymbol(HIP_SYMBOL(pkv::g_timeline), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) ==
+                   hipSuccess
+               ? 0
+               : 2;
+}
+#endif

@@ -72,3 +72,33 @@ def test_counter_summary_paths():
     assert bench.traffic_file("prefix-cascade").endswith("profiles/paged_decode_prefix-cascade_hbm_traffic.json")
     assert bench.traffic_file("chunk512-prefill").endswith("profiles/paged_prefill_chunk512_hbm_traffic.json")
 
+
+
+def test_timeline_summary_on_made_up_stamps():
+    """Two slots of waves with known stamps: the per-slot medians, the close time after the last tile and the
+    aggregate rate (all tiles of every wave, spread over its stamps) come out as constructed."""
+    n, tiles, tb = 64, 96, 4096
+    rows = np.zeros((4096, 8), dtype=np.uint64)
+    t0 = 10 ** 9
+    slot = np.arange(n) % 2
+    first = t0 + 800 + 400 * slot                       # 8 / 12 us
+    run = 10000 + 2000 * slot                           # 100 / 120 us of streaming
+    rows[:n, 0] = t0
+    rows[:n, 1] = first
+    for k in (1, 2, 3):
+        rows[:n, 1 + k] = first + run * k // 4
+    last = first + run
+    rows[:n, 5] = last + 300                            # 3 us closing the last state
+    rows[:n, 6] = slot.astype(np.uint64) | (np.uint64(5) << np.uint64(32)) | (np.uint64(tiles) << np.uint64(40))
+    rows[:n, 7] = last
+    text = bench.timeline_summary(rows, n * tiles * tb, "made up", "cmd")
+    lines = {ln.split("|")[1].strip(): ln for ln in text.splitlines() if ln.startswith("| 0 |") or ln.startswith("| 1 |")}
+    cells0 = [c.strip() for c in lines["0"].split("|")[1:-1]]
+    cells1 = [c.strip() for c in lines["1"].split("|")[1:-1]]
+    assert cells0[1] == "32" and cells0[3] == "8.0" and cells0[7] == "108.0" and cells0[9] == "111.0"
+    assert cells1[3] == "12.0" and cells1[7] == "132.0" and cells1[12] == "3.0 / 3.0 / 3.0"
+    assert "Last wave ends at 135.0" in text
+    # the rate windows add up to every tile once
+    rates = [float(ln.split("|")[2]) for ln in text.splitlines() if "–" in ln and ln.startswith("| ")]
+    total = sum(r * 1e12 * 10e-6 for r in rates)
+    assert abs(total - n * tiles * tb) / (n * tiles * tb) < 0.02
