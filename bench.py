@@ -617,8 +617,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before the timed ones (default 10; 30 with --prefill, whose matrix-bound "
-                         "calls take about 20 back-to-back calls to reach their sustained speed)")
+                    help="untimed steps before the timed ones (default 100, about 15 ms of decode steps even "
+                         "for the shortest workload, after which the clocks have settled; 30 with --prefill, whose "
+                         "matrix-bound calls take about 20 back-to-back calls to reach their sustained speed)")
     ap.add_argument("--workload", default="gqa8b", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1 = the workload's setting (0 = balanced split only)")
@@ -658,7 +659,7 @@ def main() -> int:
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
     if args.warmup is None:
-        args.warmup = 30 if args.prefill else 10
+        args.warmup = 30 if args.prefill else 100
 
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, " && ".join(args.commands), args.last)
@@ -736,21 +737,22 @@ def main() -> int:
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"resident: pools {2 * kc.numel() * kc.element_size() / 1e9:.2f} GB, workspace {ws_bytes / 1e6:.1f} MB")
 
-    def write():
-        pkv.paged_kv_write(k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
-
-    def decode():
-        if args.cascade:
-            pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, pl, pbl, w.scale, w.k_scale, w.v_scale,
-                                               partition_size=part, workspace=ws)
-        elif args.prefill:
-            pkv.paged_attention_prefill(out, q, cuq, kc, vc, bt, cl, w.scale, max_q, w.k_scale, w.v_scale)
-        elif multi:
-            pkv.paged_attention_varlen(out, q, cuq, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
-                                       partition_size=part, workspace=ws)
-        else:
-            pkv.paged_attention_decode(out, q, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
-                                       partition_size=part, workspace=ws)
+    # Each step's two launches are prepared once (arguments marshalled, C calls recorded), as a serving
+    # loop would: the timed loop then costs the host a C call per launch, so the GPU does not wait on
+    # Python between the write and the decode.
+    write = pkv.prepare(pkv.paged_kv_write, k_new, v_new, kc, vc, slots, w.k_scale, w.v_scale)
+    if args.cascade:
+        decode = pkv.prepare(pkv.paged_attention_decode_cascade, out, q, kc, vc, bt, cl, pl, pbl, w.scale,
+                             w.k_scale, w.v_scale, partition_size=part, workspace=ws)
+    elif args.prefill:
+        decode = pkv.prepare(pkv.paged_attention_prefill, out, q, cuq, kc, vc, bt, cl, w.scale, max_q,
+                             w.k_scale, w.v_scale)
+    elif multi:
+        decode = pkv.prepare(pkv.paged_attention_varlen, out, q, cuq, kc, vc, bt, cl, w.scale, w.k_scale,
+                             w.v_scale, partition_size=part, workspace=ws)
+    else:
+        decode = pkv.prepare(pkv.paged_attention_decode, out, q, kc, vc, bt, cl, w.scale, w.k_scale, w.v_scale,
+                             partition_size=part, workspace=ws)
 
     for _ in range(args.warmup):
         write()

@@ -174,6 +174,55 @@ def _check(status: int, what: str):
         raise PkvError(status, f"{what}: {_load().pkv_status_string(status).decode()}")
 
 
+# The C entry points that launch work on a stream (the rest answer queries).
+_LAUNCHES = ("paged_kv_write", "paged_attention_decode", "paged_attention_decode_noalloc",
+             "paged_attention_decode_cascade", "paged_attention_varlen", "paged_attention_prefill",
+             "paged_kv_copy_blocks", "pkv_stream_read")
+
+
+def prepare(call, *args, **kwargs):
+    """Marshal the arguments of one launching binding call once; return a function that launches it again.
+
+    `call` is one of this module's launching functions (paged_kv_write, paged_attention_decode, ...), with
+    the arguments it would take.  Its checks and argument marshalling run here, once, and its C call is
+    recorded instead of made; the returned function makes that C call (same tensors, scalars, workspace
+    and stream) and checks its status.  The tensors stay referenced by the returned function.  This is for
+    launch loops, such as one decode step per generated token, where Python's per-call marshalling would
+    otherwise keep the GPU waiting."""
+    global _load
+    real_load = _load
+    real = real_load()
+    rec = []
+
+    class _Recorder:
+        def __getattr__(self, name):
+            fn = getattr(real, name)
+            if name not in _LAUNCHES:
+                return fn
+
+            def record(*a):
+                rec.append((name, fn, a))
+                return 0
+            return record
+
+    _load = lambda: _Recorder()  # noqa: E731  (the call below looks the library up through _load)
+    try:
+        call(*args, **kwargs)
+    finally:
+        _load = real_load
+    if len(rec) != 1:
+        raise ValueError(f"{getattr(call, '__name__', call)} made {len(rec)} launching calls; prepare needs one")
+    name, fn, cargs = rec[0]
+
+    def launch():
+        st = fn(*cargs)
+        if st != 0:
+            _check(st, name)
+
+    launch.keep_alive = (args, kwargs)
+    return launch
+
+
 def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0,
                    stream=None) -> None:
     """Store new tokens' K/V at their slots (copy, or quantise into an fp8 pool)."""

@@ -99,3 +99,26 @@ def test_decode_hands_the_library_the_workspace_of_its_stream(recorder, monkeypa
     pkv.paged_attention_decode(out, q, kc, vc, bt, cl, 0.125)  # no stream: torch's current one
     assert lib.calls[-1][-1].value == 111
     assert recorder["made"][-1] == (64, recorder["current"])
+
+
+def test_prepare_records_one_call_and_replays_it(recorder, monkeypatch):
+    """prepare runs the binding's checks and marshalling once; each launch repeats the same C call."""
+    lib = FakeLib()
+    monkeypatch.setattr(pkv, "_load", lambda: lib)
+    monkeypatch.setattr(pkv, "_dev", lambda t, name: ctypes.c_void_p(t.data_ptr()))
+    B, H, Hkv, D, NB = 2, 4, 2, 64, 3
+    q = torch.full((B, H, D), 0.0)
+    out = torch.full((B, H, D), 0.0)
+    kc = torch.full(pkv.k_cache_shape(NB, Hkv, D, "f32"), 0.0)
+    vc = torch.full(pkv.v_cache_shape(NB, Hkv, D), 0.0)
+    bt = torch.full((B, 4), 0, dtype=torch.int32)
+    cl = torch.full((B,), 1, dtype=torch.int32)
+    launch = pkv.prepare(pkv.paged_attention_decode, out, q, kc, vc, bt, cl, 0.125, stream=FakeStream(444))
+    assert lib.calls == []                              # nothing launched while preparing
+    assert pkv._load() is lib                           # the library lookup is restored
+    launch()
+    launch()
+    assert len(lib.calls) == 2 and lib.calls[0] == lib.calls[1]
+    assert lib.calls[0][-1].value == 444 and lib.calls[0][0].value == out.data_ptr()
+    with pytest.raises(ValueError):                     # shape checks still run at preparation
+        pkv.prepare(pkv.paged_attention_decode, out[:1], q, kc, vc, bt, cl, 0.125)

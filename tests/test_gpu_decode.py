@@ -306,3 +306,28 @@ def test_long_context_merge_tree(gpu, hq, hkv, d, cache, part):
     want = _gpu.oracle_decode(w, w.layout, ok, ov)
     err, where = _gpu.max_err(outs[0], want)
     assert err <= _gpu.TOL[cache], (err, where)
+
+
+def test_prepared_launches_match_direct_calls(gpu):
+    """pkv.prepare: the recorded write and decode, launched three times, give the direct calls' bits."""
+    w = W.make_scaled("gqa8b", 24)
+    _gpu.note("prepared launches, gqa8b scaled")
+    kp, vp = _gpu.gpu_pools(w, w.layout, with_new=False)
+    kn, vn = _gpu.to_dev(w.new_k, w.in_dtype), _gpu.to_dev(w.new_v, w.in_dtype)
+    slots = _gpu.to_dev(w.layout.new_slots, "i32")
+    q = _gpu.to_dev(w.q, w.q_dtype)
+    bt, cl = _gpu.to_dev(w.layout.block_table, "i32"), _gpu.to_dev(w.context_lens, "i32")
+    direct = torch.empty_like(q)
+    pkv.paged_kv_write(kn, vn, kp, vp, slots, w.k_scale, w.v_scale)
+    pkv.paged_attention_decode(direct, q, kp, vp, bt, cl, w.scale, w.k_scale, w.v_scale,
+                               partition_size=w.partition_size)
+    out = torch.empty_like(q)
+    write = pkv.prepare(pkv.paged_kv_write, kn, vn, kp, vp, slots, w.k_scale, w.v_scale)
+    decode = pkv.prepare(pkv.paged_attention_decode, out, q, kp, vp, bt, cl, w.scale, w.k_scale, w.v_scale,
+                         partition_size=w.partition_size)
+    for _ in range(3):
+        out.zero_()
+        write()
+        decode()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), direct.view(torch.int16))
