@@ -175,8 +175,11 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  *                the rule M = max m_i, out = sum 2^(m_i-M) acc_i / sum
  *                2^(m_i-M) l_i (in registers within a wave, through the
  *                workspace between waves, by the last wave to finish its
- *                part; no second launch).  The split changes rounding only;
- *                for fixed sizes and lengths the result is deterministic.
+ *                part; no second launch).  Between waves a state travels as
+ *                m, l in fp32 and acc / l in the query dtype (bf16 for bf16
+ *                queries: one more rounding of a partial result, as an output
+ *                row would get).  The split changes rounding only; for fixed
+ *                sizes and lengths the result is deterministic.
  * workspace      device buffer of >= paged_attention_workspace_bytes(...)
  *                bytes, owned by the caller, 16-byte aligned, zero-filled
  *                before its first use (every call that completes leaves its
