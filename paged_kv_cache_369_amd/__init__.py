@@ -23,9 +23,10 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
-           "paged_attention_decode_noalloc",
+           "paged_attention_decode_noalloc", "paged_attention_decode_cascade", "prepare",
            "BlockManager", "paged_kv_copy_blocks", "paged_attention_varlen", "paged_attention_prefill",
            "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
@@ -46,8 +47,14 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+_RECORDING = threading.local()  # prepare(): this thread's recorder, which stands in for the library
+
+
 def _load():
     global _lib
+    rec = getattr(_RECORDING, "lib", None)
+    if rec is not None:
+        return rec
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
@@ -189,9 +196,7 @@ def prepare(call, *args, **kwargs):
     and stream) and checks its status.  The tensors stay referenced by the returned function.  This is for
     launch loops, such as one decode step per generated token, where Python's per-call marshalling would
     otherwise keep the GPU waiting."""
-    global _load
-    real_load = _load
-    real = real_load()
+    real = _load()
     rec = []
 
     class _Recorder:
@@ -205,11 +210,11 @@ def prepare(call, *args, **kwargs):
                 return 0
             return record
 
-    _load = lambda: _Recorder()  # noqa: E731  (the call below looks the library up through _load)
+    _RECORDING.lib = _Recorder()  # the call below looks the library up through _load, in this thread
     try:
         call(*args, **kwargs)
     finally:
-        _load = real_load
+        _RECORDING.lib = None
     if len(rec) != 1:
         raise ValueError(f"{getattr(call, '__name__', call)} made {len(rec)} launching calls; prepare needs one")
     name, fn, cargs = rec[0]

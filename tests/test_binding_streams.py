@@ -104,7 +104,7 @@ def test_decode_hands_the_library_the_workspace_of_its_stream(recorder, monkeypa
 def test_prepare_records_one_call_and_replays_it(recorder, monkeypatch):
     """prepare runs the binding's checks and marshalling once; each launch repeats the same C call."""
     lib = FakeLib()
-    monkeypatch.setattr(pkv, "_load", lambda: lib)
+    monkeypatch.setattr(pkv, "_lib", lib)
     monkeypatch.setattr(pkv, "_dev", lambda t, name: ctypes.c_void_p(t.data_ptr()))
     B, H, Hkv, D, NB = 2, 4, 2, 64, 3
     q = torch.full((B, H, D), 0.0)
