@@ -208,7 +208,6 @@ constexpr unsigned kRawBufferWord3 = 0x00020000u;
 // 16-byte access, and the four lanes of a column fill one 64-byte line per
 // access (lane (col, g) at col * D + 16 c + 8 g), so that the stores, which
 // write through, are whole lines.
-
 // Two chunks of a state's acc as stored in a bf16 slot (acc * inv, rounded to
 // nearest even), and back (times l).
 __device__ __forceinline__ u32x4 slot_pack(const f32x4& a, const f32x4& b, float inv) {
