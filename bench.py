@@ -567,7 +567,7 @@ def timeline_summary(rows, kv_bytes: int, desc: str, command: str) -> str:
     n = len(r)
     out = [f"# Per-wave timeline of one decode call, {desc}", "",
            "Command (run from the repository root; the instrumented library is the same sources with "
-           "PKV_TIMELINE defined, each wave adding six clock reads and one 64-byte store):", "",
+           "PKV_TIMELINE defined, each wave adding seven clock reads and one 64-byte store):", "",
            f"    {command}", "",
            f"{n} waves with a stretch; times in µs after the first wave's entry (real-time clock, 100 MHz). "
            f"Last wave ends at {end.max():.1f} µs.", "",
