@@ -239,6 +239,54 @@ def plain_read(torch, pkv, nbytes: int, reps: int = 10) -> dict:
             "kernel": "pkv_stream_read over a buffer of the decode's KV size (a plain streaming read)"}
 
 
+READ_PROBE_CASES = [(2048, 4, 3), (2048, 8, 3), (2048, 16, 3), (2048, 4, 4), (2048, 16, 4),
+                    (4096, 4, 2), (4096, 8, 2), (4096, 16, 2)]
+
+
+def read_probe(torch, pkv, out_path: str, reps: int = 20) -> int:
+    """Markdown table of pkv_tile_read (the decode's gathered K/V tile reads, no arithmetic) over 800 MB per
+    launch (two 400 MB pools, a shuffled list of every tile), for each supported tile size, V load width and
+    depth, next to pkv_stream_read over the same 800 MB.  Events around `reps` launches after three warm-ups."""
+    pool = 400 << 20
+    k = torch.ones(pool // 4, dtype=torch.int32, device="cuda")
+    v = torch.ones(pool // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(pkv.TILE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    gen = torch.Generator().manual_seed(7)
+    rows = ["| tile (K + V) | V load width | tiles in flight | µs per launch | GB/s |", "|---|---|---|---|---|"]
+    for tb, vw, depth in READ_PROBE_CASES:
+        n = pool // tb
+        ids = torch.randperm(n, generator=gen).to(torch.int32).cuda()
+        for _ in range(3):
+            pkv.pkv_tile_read(k, v, ids, n, tb, vw, depth, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pkv.pkv_tile_read(k, v, ids, n, tb, vw, depth, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        kind = "fp8, D=128" if tb == 2048 else "bf16, D=128"
+        rows.append(f"| {tb // 1024} KiB + {tb // 1024} KiB ({kind}) | {vw} B | {depth} | {us:.1f} | "
+                    f"{2 * pool / us / 1e3:.0f} |")
+    del k, v
+    pr = plain_read(torch, pkv, 2 * pool, reps)
+    rows.append(f"| plain streaming read (`pkv_stream_read`, 16 B) | — | 4 per thread | {pr['avg_us']:.1f} | "
+                f"{pr['GBps']:.0f} |")
+    text = "\n".join([
+        "# Gathered K/V tile reads on MI355X (the decode's stream without its arithmetic)", "",
+        "Command (run from the repository root):", "",
+        "    python3 bench.py --read-probe", "",
+        "`pkv_tile_read`: 2048 one-wave workgroups (the decode's occupancy for bf16 and fp8 at head_dim 128), "
+        "each reading an equal share of a shuffled list of every tile id, the K tile and then the V tile of each, "
+        "with nontemporal loads; K by 16-byte lane loads, V by the width given.  800 MB per launch "
+        f"(two 400 MB pools), the mean of {reps} launches after three warm-ups.", ""] + rows) + "\n"
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+    return 0
+
+
 def _csv_rows(directory: str, suffix: str):
     files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
     if not files:
@@ -641,6 +689,10 @@ def main() -> int:
                     help="run the instrumented library (python -m paged_kv_cache_369_amd.build --timeline) and "
                          "write a per-wave timeline summary of one decode call to --timeline-out")
     ap.add_argument("--timeline-out", default=None, help="where --timeline writes (default profiles/)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="time pkv_tile_read (gathered K/V tile reads) per tile size, V load width and depth, and "
+                         "write profiles/read_probe_tiles.md")
+    ap.add_argument("--read-probe-out", default=None, help="where --read-probe writes (default profiles/)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode step, run a plain device copy of known size (counter scale)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a markdown summary of a rocprofv3 --stats run")
@@ -693,6 +745,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration(torch, args.steps)
+    if args.read_probe:
+        return read_probe(torch, pkv, args.read_probe_out or os.path.join(PROFILES, "read_probe_tiles.md"))
 
     t0 = time.perf_counter()
     w = W.make(args.workload, args.seed)

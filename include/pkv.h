@@ -91,7 +91,8 @@ typedef enum pkv_status {
  *   9 = paged_attention_decode_noalloc and PKV_ERR_SCRATCH;
  *  10 = the shared-prefix decode merges prefix and suffix states in a second
  *       launch: the workspace loses its meeting counters (every workspace is
- *       1 MiB smaller) and the num_seqs * runs limit of the cascade is gone. */
+ *       1 MiB smaller) and the num_seqs * runs limit of the cascade is gone;
+ *  11 = pkv_tile_read (a measurement aid). */
 int pkv_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (host). */
@@ -408,6 +409,28 @@ int paged_attention_prefill(void* out,
  */
 #define PKV_STREAM_SINK_WORDS 8192
 int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * pkv_tile_read -- the decode's read pattern without its arithmetic: 2048
+ * one-wave workgroups each read an equal share of the list `ids` (n entries),
+ * and for each entry the tile of `tile_bytes` at index id of `k`, then the
+ * one at index id of `v`, with `depth` tiles in flight and nontemporal loads:
+ * K by 16-byte lane loads, V by `v_load_bytes`-byte ones.  An id outside
+ * [0, num_tiles) reads tile 0 or num_tiles - 1 (the reads stay in the
+ * pools).  `sink` is a device array of PKV_TILE_SINK_WORDS uint32 owned by
+ * the caller; the kernel may write any of them (in practice none).  A
+ * measurement aid: it sets the V load widths, the depth and the tile size of
+ * the decode's stream side by side.  Asynchronous on `stream`.
+ * Supported (tile_bytes, v_load_bytes, depth): 2048 with (4, 8 or 16, 3) or
+ * (4 or 16, 4) -- fp8 tiles of head_dim 128; 4096 with (4, 8 or 16, 2) --
+ * bf16 tiles of head_dim 128; otherwise PKV_ERR_UNSUPPORTED.
+ * Errors: PKV_ERR_INVALID_ARG (n or num_tiles < 0; NULL pointers or
+ * num_tiles == 0 with n > 0), PKV_ERR_ALIGNMENT (k or v not 16-aligned, ids
+ * or sink not 4-aligned), PKV_ERR_HIP.  n == 0 is a no-op.
+ */
+#define PKV_TILE_SINK_WORDS 2048
+int pkv_tile_read(const void* k, const void* v, const int32_t* ids, int32_t n, int32_t num_tiles,
+                  int32_t tile_bytes, int32_t v_load_bytes, int32_t depth, uint32_t* sink, void* stream);
 
 /*
  * pkv_check_inputs -- count the contents of the index arrays that the kernels

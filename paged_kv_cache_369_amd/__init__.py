@@ -28,7 +28,7 @@ import threading
 __all__ = ["paged_kv_write", "paged_attention_decode", "paged_attention_workspace_bytes", "pkv_check_inputs",
            "paged_attention_decode_noalloc", "paged_attention_decode_cascade", "prepare",
            "BlockManager", "paged_kv_copy_blocks", "paged_attention_varlen", "paged_attention_prefill",
-           "pkv_abi_version", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
+           "pkv_abi_version", "pkv_stream_read", "pkv_tile_read", "PkvError", "library_path", "BLOCK_SIZE", "k_cache_shape", "v_cache_shape"]
 
 BLOCK_SIZE = 16
 _ELT = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -89,6 +89,8 @@ def _load():
     lib.paged_attention_prefill.restype = ctypes.c_int
     lib.pkv_stream_read.argtypes = [p, sz, p, p]
     lib.pkv_stream_read.restype = ctypes.c_int
+    lib.pkv_tile_read.argtypes = [p, p, p, i32, i32, i32, i32, i32, p, p]
+    lib.pkv_tile_read.restype = ctypes.c_int
     lib.pkv_check_inputs.argtypes = [p, i32, p, i32, p, i32, i32, p, p]
     lib.pkv_check_inputs.restype = ctypes.c_int
     i64 = ctypes.c_int64
@@ -435,6 +437,19 @@ def pkv_stream_read(buf, sink, stream=None) -> None:
         raise ValueError(f"sink needs {STREAM_SINK_WORDS} 32-bit words")
     st = lib.pkv_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"), _stream(stream))
     _check(st, "pkv_stream_read")
+
+
+TILE_SINK_WORDS = 2048  # PKV_TILE_SINK_WORDS
+
+
+def pkv_tile_read(k, v, ids, num_tiles: int, tile_bytes: int, v_load_bytes: int, depth: int, sink,
+                  stream=None) -> None:
+    """The decode's read pattern without its arithmetic (see include/pkv.h): the K then V tile of each entry
+    of `ids` from the byte pools `k` and `v` (num_tiles tiles each), V read by v_load_bytes-byte loads."""
+    lib = _load()
+    st = lib.pkv_tile_read(_dev(k, "k"), _dev(v, "v"), _dev(ids, "ids"), ids.numel(), int(num_tiles),
+                           int(tile_bytes), int(v_load_bytes), int(depth), _dev(sink, "sink"), _stream(stream))
+    _check(st, "pkv_tile_read")
 
 
 def pkv_check_inputs(num_blocks: int, block_table=None, context_lens=None, slot_mapping=None, stream=None):

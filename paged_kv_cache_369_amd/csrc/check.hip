@@ -179,3 +179,113 @@ extern "C" int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, vo
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), int64_t(bytes / 16), sink);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
+
+// ---- a gathered-tile read (measurement aid) ----
+//
+// The decode's access pattern without its arithmetic: 2048 one-wave
+// workgroups (two per SIMD, the decode's occupancy for bf16 and fp8 at
+// head_dim 128) each read an equal share of a list of tile ids, K tile then V
+// tile of each id from two pools, `depth` tiles in flight, nontemporal loads.
+// K is read with 16-byte lane loads and V with 4-, 8- or 16-byte ones, so
+// the rate of each V load width can be set beside the others.  Each wave
+// folds what it read into one word, stored only if it matches a constant.
+namespace pkv {
+namespace {
+
+constexpr int kTileReadWaves = 2048;
+
+template <int VW>
+struct TileWord;
+template <>
+struct TileWord<4> {
+    typedef uint32_t T;
+    __device__ static uint32_t fold(T x) { return x; }
+};
+template <>
+struct TileWord<8> {
+    typedef unsigned T __attribute__((ext_vector_type(2)));
+    __device__ static uint32_t fold(T x) { return x[0] ^ x[1]; }
+};
+template <>
+struct TileWord<16> {
+    typedef unsigned T __attribute__((ext_vector_type(4)));
+    __device__ static uint32_t fold(T x) { return x[0] ^ x[1] ^ x[2] ^ x[3]; }
+};
+
+template <int TILE, int VW, int P>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tile_read_kernel(
+    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v, const int32_t* __restrict__ ids, int32_t n,
+    int32_t num_tiles, uint32_t* sink) {
+    constexpr int NK = TILE / 1024, NV = TILE / (64 * VW);
+    typedef typename TileWord<16>::T K16;
+    typedef typename TileWord<VW>::T VT;
+    const int lane = threadIdx.x;
+    const int64_t w = blockIdx.x, nw = gridDim.x;
+    const int64_t lo = w * n / nw, hi = (w + 1) * n / nw;
+    if (lo >= hi) return;
+    K16 kb[P][NK];
+    VT vb[P][NV];
+    uint32_t acc = 0;
+    auto issue = [&](int s, int64_t pos) {
+        int id = ids[pos < hi ? pos : lo];
+        id = id < 0 ? 0 : (id >= num_tiles ? num_tiles - 1 : id);  // any contents stay in the pools
+        const uint8_t* kp = k + int64_t(id) * TILE + lane * 16;
+        const uint8_t* vp = v + int64_t(id) * TILE + lane * VW;
+#pragma unroll
+        for (int u = 0; u < NK; ++u) kb[s][u] = __builtin_nontemporal_load(reinterpret_cast<const K16*>(kp + u * 1024));
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+            vb[s][u] = __builtin_nontemporal_load(reinterpret_cast<const VT*>(vp + u * 64 * VW));
+    };
+#pragma unroll
+    for (int s = 0; s < P - 1; ++s) issue(s, lo + s);
+    for (int64_t t = lo; t < hi; t += P) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            if (t + s < hi) {
+                issue((s + P - 1) % P, t + s + P - 1);
+#pragma unroll
+                for (int u = 0; u < NK; ++u) acc ^= TileWord<16>::fold(kb[s][u]);
+#pragma unroll
+                for (int u = 0; u < NV; ++u) acc ^= TileWord<VW>::fold(vb[s][u]);
+            }
+        }
+    }
+    if (acc == 0x9e3779b9u) sink[w] = acc;
+}
+
+template <int TILE, int VW, int P>
+hipError_t tile_read_t(const void* k, const void* v, const int32_t* ids, int32_t n, int32_t num_tiles, uint32_t* sink,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL((tile_read_kernel<TILE, VW, P>), dim3(kTileReadWaves), dim3(64), 0, stream,
+                       static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), ids, n, num_tiles, sink);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_tile_read(const void* k, const void* v, const int32_t* ids, int32_t n, int32_t num_tiles,
+                             int32_t tile_bytes, int32_t v_load_bytes, int32_t depth, uint32_t* sink, void* stream) {
+    if (n < 0 || num_tiles < 0) return PKV_ERR_INVALID_ARG;
+    if (n == 0) return PKV_OK;
+    if (!k || !v || !ids || !sink || num_tiles == 0) return PKV_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(k) & 15) || (reinterpret_cast<uintptr_t>(v) & 15) ||
+        (reinterpret_cast<uintptr_t>(ids) & 3) || (reinterpret_cast<uintptr_t>(sink) & 3))
+        return PKV_ERR_ALIGNMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipErrorInvalidValue;
+    const int key = tile_bytes * 1000 + v_load_bytes * 10 + depth;
+    switch (key) {
+        case 2048 * 1000 + 40 + 3: e = pkv::tile_read_t<2048, 4, 3>(k, v, ids, n, num_tiles, sink, s); break;
+        case 2048 * 1000 + 80 + 3: e = pkv::tile_read_t<2048, 8, 3>(k, v, ids, n, num_tiles, sink, s); break;
+        case 2048 * 1000 + 160 + 3: e = pkv::tile_read_t<2048, 16, 3>(k, v, ids, n, num_tiles, sink, s); break;
+        case 2048 * 1000 + 40 + 4: e = pkv::tile_read_t<2048, 4, 4>(k, v, ids, n, num_tiles, sink, s); break;
+        case 2048 * 1000 + 160 + 4: e = pkv::tile_read_t<2048, 16, 4>(k, v, ids, n, num_tiles, sink, s); break;
+        case 4096 * 1000 + 40 + 2: e = pkv::tile_read_t<4096, 4, 2>(k, v, ids, n, num_tiles, sink, s); break;
+        case 4096 * 1000 + 80 + 2: e = pkv::tile_read_t<4096, 8, 2>(k, v, ids, n, num_tiles, sink, s); break;
+        case 4096 * 1000 + 160 + 2: e = pkv::tile_read_t<4096, 16, 2>(k, v, ids, n, num_tiles, sink, s); break;
+        default: return PKV_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

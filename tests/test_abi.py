@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 10
+    assert lib.pkv_abi_version() == 11
     # the header's version history names every version up to the current one
     text = open(HEADER).read()
     hist = text[text.index("Version of this ABI"):text.index("int pkv_abi_version(void);")]
@@ -271,3 +271,24 @@ def test_stream_read_validation(lib):
     assert lib.pkv_stream_read(A + 8, 64, A, None) == ALIGN
     assert lib.pkv_stream_read(A, 72, A, None) == ALIGN
     assert lib.pkv_stream_read(A, 64, A + 2, None) == ALIGN
+
+
+def test_tile_read_validation(lib):
+    f = ctypes.CDLL(pkv.library_path()).pkv_tile_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def call(k=A, v=A, ids=A, n=16, nt=8, tb=2048, vw=4, p=3, sink=A):
+        return f(k, v, ids, n, nt, tb, vw, p, sink, None)
+    assert call(n=0) == OK                                      # nothing to read: no launch
+    assert call(n=-1) == INVALID and call(nt=-1) == INVALID
+    assert call(nt=0) == INVALID
+    for bad in ("k", "v", "ids", "sink"):
+        assert call(**{bad: 0}) == INVALID
+    assert call(k=A + 8) == ALIGN and call(v=A + 4) == ALIGN
+    assert call(ids=A + 2) == ALIGN and call(sink=A + 1) == ALIGN
+    assert call(tb=1024) == UNSUPPORTED                          # only the decode's tile sizes
+    assert call(vw=2) == UNSUPPORTED
+    assert call(tb=4096, vw=4, p=3) == UNSUPPORTED               # bf16 tiles run two deep
+    assert call(tb=2048, vw=8, p=4) == UNSUPPORTED
