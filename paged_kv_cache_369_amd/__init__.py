@@ -446,7 +446,15 @@ def pkv_tile_read(k, v, ids, num_tiles: int, tile_bytes: int, v_load_bytes: int,
                   stream=None) -> None:
     """The decode's read pattern without its arithmetic (see include/pkv.h): the K then V tile of each entry
     of `ids` from the byte pools `k` and `v` (num_tiles tiles each), V read by v_load_bytes-byte loads."""
+    import torch
     lib = _load()
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    if sink.numel() * sink.element_size() < 4 * TILE_SINK_WORDS:
+        raise ValueError(f"sink must hold {TILE_SINK_WORDS} 32-bit words")
+    for name, t in (("k", k), ("v", v)):
+        if t.numel() * t.element_size() < int(num_tiles) * int(tile_bytes):
+            raise ValueError(f"{name} holds fewer than num_tiles tiles of tile_bytes")
     st = lib.pkv_tile_read(_dev(k, "k"), _dev(v, "v"), _dev(ids, "ids"), ids.numel(), int(num_tiles),
                            int(tile_bytes), int(v_load_bytes), int(depth), _dev(sink, "sink"), _stream(stream))
     _check(st, "pkv_tile_read")

@@ -98,3 +98,25 @@ def test_check_repeats_at_chunk_sizes(gpu, case):
     _gpu.note(f"check_inputs repeats case={case} T={T} want={want}")
     got = pkv.pkv_check_inputs(NB, _gpu.to_dev(bt, "i32"), _gpu.to_dev(cl, "i32"), _gpu.to_dev(slots, "i32"))
     assert got == want
+
+
+def test_tile_read_every_case_and_any_ids(gpu):
+    """The tile-read measurement aid runs every supported (tile, V width, depth), keeps ids outside the pool
+    inside it, and for zero-filled pools writes nothing to its sink."""
+    import bench
+    nt = 96
+    k = torch.zeros(nt * 4096 // 4, dtype=torch.int32, device="cuda")
+    v = torch.zeros(nt * 4096 // 4, dtype=torch.int32, device="cuda")
+    ids = torch.tensor([0, 5, -7, 95, 96, 1 << 30] * 700, dtype=torch.int32, device="cuda")  # some outside
+    sink = torch.full((pkv.TILE_SINK_WORDS,), -1, dtype=torch.int32, device="cuda")
+    for tb, vw, depth in bench.READ_PROBE_CASES:
+        _gpu.note(f"tile read tb={tb} vw={vw} depth={depth}")
+        pkv.pkv_tile_read(k, v, ids, nt * 4096 // tb, tb, vw, depth, sink)
+        torch.cuda.synchronize()
+    assert bool((sink == -1).all())
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_tile_read(k, v, ids, nt, 2048, 8, 4, sink)             # not a supported case
+    with pytest.raises(ValueError):
+        pkv.pkv_tile_read(k, v, ids, nt, 4096, 4, 2, torch.zeros(16, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        pkv.pkv_tile_read(k, v, ids, 4 * nt, 4096, 4, 2, sink)          # pools smaller than num_tiles tiles
